@@ -1,0 +1,118 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact-attention library, libfa.so.
+ *
+ * The operation is standard scaled dot-product attention computed without ever
+ * writing the N x N score or probability matrices to memory:
+ *
+ *     S = scale * Q K^T,   P = softmax(S) (row-wise),   O = P V,
+ *     LSE_i = m_i + ln(l_i),  m_i = max_j S_ij,  l_i = sum_j exp(S_ij - m_i).
+ *
+ * The problem statement is the one in "FlashAttention 硬件感知计算剖析" (section 一.2,
+ * the three formulas of standard attention); tensors are laid out as
+ * [Batch, Heads, Seq_Len, Head_Dim] as in that page's section 五.1; the running
+ * row statistics m (max) and l (exp-sum) and the rescale by exp(m_old - m_new) are
+ * the online softmax of "从零理解Flash Attention中的online softmax" (section 3.1) and
+ * of the two-block merge in "FlashAttention 硬件感知计算剖析" (section 二).  The saved
+ * statistic is the log-sum-exp m + ln l, which is what a recompute-based backward
+ * ("从原理出发理解 Flash Attention Part2", section 2.4) needs to rebuild P.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a HIP device pointer owned by the caller.  The
+ *     library allocates nothing in these calls and keeps no pointer after return.
+ *     Buffers must stay alive until the work queued on `stream` has completed.
+ *   - Layout: contiguous [B, H, N, d]; element (b, h, n, k) is at index
+ *     ((b*H + h)*N + n)*d + k.  LSE / D are contiguous fp32 [B, H, N].
+ *   - Q, K, V, O (and dO, dQ, dK, dV) share one element type `dtype`; O has the
+ *     input dtype.  LSE is always fp32, natural log.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous: validation errors return synchronously before any
+ *     work is queued; device faults surface at the caller's next synchronisation.
+ *   - Outputs must not alias inputs.  Tensor pointers must be 16-byte aligned,
+ *     LSE/D 4-byte aligned.
+ *   - Non-finite inputs propagate to the outputs; finite inputs of any magnitude
+ *     give finite outputs.
+ *   - Validation order: shapes, head dim / dtype; then an empty problem
+ *     (B*H*N == 0) returns FA_OK and queues nothing (its pointers may be NULL);
+ *     then null pointers, alignment, scale, and finally the device.
+ *   - Thread safety: calls may be made concurrently from several host threads;
+ *     the only global state is a read-only per-device property cache.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_F32 = 0,
+    FA_F16 = 1,
+    FA_BF16 = 2
+} fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    FA_ERR_SHAPE = 2,       /* B, H or N negative, or sizes overflow the index math */
+    FA_ERR_UNSUPPORTED = 3, /* head dim not in {64, 128}, or unknown dtype           */
+    FA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte (LSE: 4-byte) aligned */
+    FA_ERR_SCALE = 5,       /* scale is not finite or not > 0                        */
+    FA_ERR_DEVICE = 6,      /* no HIP device, or the current device is not gfx950    */
+    FA_ERR_LAUNCH = 7,      /* the kernel launch was rejected by the runtime          */
+    FA_ERR_WORKSPACE = 8    /* workspace missing or smaller than required             */
+} fa_status;
+
+/* Launch plan the tile/occupancy chooser picks for a forward problem. */
+typedef struct {
+    int32_t block_q;        /* Br: query rows per workgroup                            */
+    int32_t block_k;        /* Bc: keys per K/V tile streamed through LDS              */
+    int32_t waves;          /* wavefronts (64 lanes) per workgroup                     */
+    int32_t rows_per_wave;  /* query rows owned by each wave                           */
+    int32_t lds_bytes;      /* LDS per workgroup (K and V tiles, double-buffered)      */
+    int64_t grid;           /* workgroups launched = B*H*ceil(N/Br) (*splits)          */
+    int32_t kv_splits;      /* >1: key range split across workgroups, then merged      */
+    int32_t reserved;
+} fa_plan;
+
+/*
+ * Forward attention.  Q, K, V: [B,H,N,d] of `dtype`; O: [B,H,N,d] of `dtype`;
+ * LSE: [B,H,N] fp32 (natural log).  `scale` multiplies Q K^T (1/sqrt(d) for the
+ * usual attention).  Supported: d in {64, 128}; dtype FA_BF16 / FA_F16 (matrix
+ * products on bf16/fp16 MFMA with fp32 accumulation and fp32 softmax statistics)
+ * or FA_F32 (fp32 MFMA throughout).  Any N >= 0 (tails are masked).
+ */
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                 fa_dtype dtype, void* stream);
+
+/*
+ * Causal forward: as fa_fwd, but query i attends only to keys j <= i (the
+ * lower-triangular mask of "FlashAttention 硬件感知计算剖析", section 五.3).  Key
+ * tiles strictly above the diagonal are skipped, not masked.
+ */
+fa_status fa_fwd_causal(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                        fa_dtype dtype, void* stream);
+
+/*
+ * The plan fa_fwd / fa_fwd_causal would launch for this problem on a gfx950
+ * device (pure host computation: no HIP call, usable without a GPU).
+ * Returns the same validation status fa_fwd would (pointer checks excepted).
+ */
+fa_status fa_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype,
+                      int causal, fa_plan* plan);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_str(fa_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

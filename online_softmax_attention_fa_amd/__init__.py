@@ -1,0 +1,161 @@
+"""Python binding of libfa.so (the MI355X fused attention library).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+behind the C ABI declared in ``include/fa.h``.  PyTorch supplies device memory and
+the stream; this module turns tensors into pointers and sizes, calls the C entry
+point of the same name, and raises on a non-OK status.  If ``libfa.so`` has not
+been built the calls raise -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+
+STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_ALIGN",
+    5: "FA_ERR_SCALE", 6: "FA_ERR_DEVICE", 7: "FA_ERR_LAUNCH", 8: "FA_ERR_WORKSPACE",
+}
+
+# Every symbol include/fa.h declares.
+EXPORTS = ("fa_fwd", "fa_fwd_causal", "fa_fwd_plan", "fa_status_str", "fa_version")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("waves", ctypes.c_int32),
+        ("rows_per_wave", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("grid", ctypes.c_int64),
+        ("kv_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so once; raises FileNotFoundError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is not built; run __graft_entry__.build() or "
+                                f"python -m online_softmax_attention_fa_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I64, F, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    fwd_args = [P, P, P, P, P, I64, I64, I64, I64, F, I, P]
+    for name in ("fa_fwd", "fa_fwd_causal"):
+        getattr(lib, name).argtypes = fwd_args
+        getattr(lib, name).restype = I
+    lib.fa_fwd_plan.argtypes = [I64, I64, I64, I64, I, I, ctypes.POINTER(Plan)]
+    lib.fa_fwd_plan.restype = I
+    lib.fa_status_str.argtypes = [I]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = I
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    try:
+        return load().fa_status_str(status).decode()
+    except FileNotFoundError:
+        return STATUS.get(status, f"status {status}")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise FaError(status, where)
+
+
+def dtype_code(torch_dtype) -> int:
+    import torch
+
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if torch_dtype not in codes:
+        raise TypeError(f"unsupported dtype {torch_dtype}")
+    return codes[torch_dtype]
+
+
+def _stream_handle(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_qkv(q, k, v):
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v must share one dtype")
+
+
+def fa_fwd(q, k, v, o=None, lse=None, scale=None, stream=None, causal=False):
+    """O, LSE = attention(q, k, v) through ``fa_fwd`` (or ``fa_fwd_causal``).
+
+    q, k, v: contiguous device tensors [B, H, N, d] (fp32 / fp16 / bf16).
+    o, lse: optional preallocated outputs ([B,H,N,d] input dtype, [B,H,N] fp32).
+    scale: defaults to 1/sqrt(d).  Returns (o, lse).
+    """
+    import torch
+
+    lib = load()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("o must be contiguous, shaped and typed like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    fn = lib.fa_fwd_causal if causal else lib.fa_fwd
+    with torch.cuda.device(q.device):
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                B, H, N, d, float(scale), dtype_code(q.dtype), _stream_handle(stream))
+    _check(st, "fa_fwd_causal" if causal else "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_causal(q, k, v, o=None, lse=None, scale=None, stream=None):
+    return fa_fwd(q, k, v, o=o, lse=lse, scale=scale, stream=stream, causal=True)
+
+
+def fa_fwd_plan(B, H, N, d, dtype, causal=False) -> dict:
+    """The launch plan the library's chooser picks (pure host computation)."""
+    lib = load()
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    plan = Plan()
+    _check(lib.fa_fwd_plan(B, H, N, d, code, int(bool(causal)), ctypes.byref(plan)), "fa_fwd_plan")
+    return plan.as_dict()
+
+
+def fa_version() -> int:
+    return load().fa_version()

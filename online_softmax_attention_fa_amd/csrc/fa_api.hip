@@ -1,0 +1,128 @@
+// C ABI of libfa.so: argument validation, the launch plan, device checks, dispatch.
+// Every validation step runs before any HIP call, so the error paths work (and are
+// tested) on a machine without a GPU.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <mutex>
+#include <string.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    std::once_flag once;
+    bool gfx950 = false;
+};
+DeviceInfo g_devices[kMaxDevices];
+
+// FA_OK if the calling thread's current HIP device is a gfx950.
+fa_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return FA_ERR_DEVICE;
+    }
+    DeviceInfo& info = g_devices[dev];
+    std::call_once(info.once, [&] {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
+            info.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        (void)hipGetLastError();
+    });
+    return info.gfx950 ? FA_OK : FA_ERR_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape / dtype checks shared by the plan query and the launches.
+fa_status check_problem(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    // per-head element offsets are 32-bit inside the kernels; grid is 32-bit
+    if (N > 0 && N * d >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+    if (B > 0 && H > (int64_t(1) << 31) / B) return FA_ERR_SHAPE;
+    const int64_t bh = B * H;
+    if (bh > 0 && N > 0 && bh * fa::ceil_div(N, 128) >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
+                     void* stream, int causal) {
+    fa_status st = check_problem(B, H, N, d, dtype);
+    if (st != FA_OK) return st;
+    if (B * H * N == 0) return FA_OK;   // empty tensors may carry NULL data pointers
+    if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
+        return FA_ERR_ALIGN;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+    st = check_device();
+    if (st != FA_OK) return st;
+
+    const fa_plan plan = fa::choose_fwd_plan(B, H, N, d, dtype, causal);
+    fa::FwdArgs a;
+    a.q = Q;
+    a.k = K;
+    a.v = V;
+    a.o = O;
+    a.lse = LSE;
+    a.n = (int)N;
+    a.n_qblk = (int)fa::ceil_div(N, plan.block_q);
+    a.n_blocks = (int)plan.grid;
+    a.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+    const int e = fa_launch_fwd(a, plan, dtype, (int)d, causal, stream);
+    return e == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                 fa_dtype dtype, void* stream) {
+    return fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, dtype, stream, 0);
+}
+
+fa_status fa_fwd_causal(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                        fa_dtype dtype, void* stream) {
+    return fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, dtype, stream, 1);
+}
+
+fa_status fa_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype, int causal,
+                      fa_plan* plan) {
+    if (!plan) return FA_ERR_NULL;
+    fa_status st = check_problem(B, H, N, d, dtype);
+    if (st != FA_OK) return st;
+    memset(plan, 0, sizeof(*plan));
+    if (B * H * N == 0) return FA_OK;
+    *plan = fa::choose_fwd_plan(B, H, N, d, dtype, causal);
+    return FA_OK;
+}
+
+const char* fa_status_str(fa_status s) {
+    switch (s) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative or too large B/H/N";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128, dtype f32/f16/bf16";
+        case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensors need 16-byte alignment (LSE 4-byte)";
+        case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+        case FA_ERR_DEVICE: return "FA_ERR_DEVICE: no HIP device or the current device is not gfx950";
+        case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    }
+    return "FA_ERR_UNKNOWN";
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Internal declarations shared by the C ABI (fa_api.hip) and the kernels.
+//
+// The tile / occupancy chooser lives here as a pure host function so that the
+// library can report its plan without a GPU (fa_fwd_plan) and the CPU tests can
+// check it.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/fa.h"
+
+namespace fa {
+
+// Kernel arguments of the forward pass (passed by value).
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int n;          // sequence length N
+    int n_qblk;     // ceil(N / Br)
+    int n_blocks;   // workgroups in the grid = B*H*n_qblk
+    float c;        // scale * log2(e): scores are taken to base 2 inside the kernel
+};
+
+// Kernel variants compiled into the library.  kind: 0 = fp32, 1 = fp16, 2 = bf16.
+struct FwdVariant {
+    int dtype;      // fa_dtype
+    int d;          // head dim
+    int rows_per_wave;
+    int block_k;
+    int waves;
+};
+
+constexpr int kWaveSize = 64;
+constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kCus = 256;
+constexpr int kLdsPerCu = 160 * 1024;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// LDS bytes of one forward workgroup: K tile and transposed V tile, two stages.
+inline int fwd_lds_bytes(int dtype, int d, int block_k) {
+    const int elt = dtype == FA_F32 ? 4 : 2;
+    if (dtype == FA_F32) {
+        // K and V tiles padded by one element per row, single stage
+        return 2 * block_k * (d + 1) * elt;
+    }
+    return 2 * (2 * block_k * d * elt);
+}
+
+// The chooser.  Inputs are already validated (d in {64,128}, dtype known, N > 0).
+//
+// bf16/fp16: 4 waves per workgroup, one wave per SIMD, 32 query rows per wave
+// (one 32-row MFMA column block), Br = 128.  Bc = 64 keys per LDS stage at
+// d = 128 and 128 at d = 64 (so a K or V stage is 16 KiB either way; 64 KiB with
+// double buffering, well inside the 160 KiB of a CU).
+// fp32: 4 waves x 32 rows, Bc = 32, single-stage LDS (latency-bound sizes only).
+inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal) {
+    fa_plan p{};
+    p.waves = 4;
+    p.kv_splits = 1;
+    if (dtype == FA_F32) {
+        p.rows_per_wave = 32;
+        p.block_k = 32;
+    } else {
+        p.block_k = d == 128 ? 64 : 128;
+        p.rows_per_wave = 32;
+    }
+    p.block_q = p.waves * p.rows_per_wave;
+    p.lds_bytes = fwd_lds_bytes(dtype, (int)d, p.block_k);
+    p.grid = B * H * ceil_div(N, p.block_q);
+    (void)causal;
+    return p;
+}
+
+}  // namespace fa
+
+// Launchers implemented in fa_fwd_kernel.hip.  Return 0 on success or the
+// hipError_t of the launch.
+int fa_launch_fwd(const fa::FwdArgs& a, const fa_plan& plan, int dtype, int d, int causal,
+                  void* stream);

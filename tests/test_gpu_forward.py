@@ -1,0 +1,155 @@
+"""GPU parity of the forward pass (through the C ABI) against the fp64 oracle.
+
+Full outputs where the oracle finishes in seconds; sampled rows (every column of O
+and LSE for 64 rows per head: tile-boundary rows plus seeded random ones) at the
+large sizes, launched exactly as the benchmark launches them.
+"""
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from gpu_util import compare, run_fwd, scale_of, to_device, to_host
+from oracle import attention_forward, attention_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_full(q, k, v, scale, causal=False):
+    B, H = q.shape[:2]
+    O = np.empty_like(q)
+    L = np.empty(q.shape[:3])
+    for b in range(B):
+        for h in range(H):
+            O[b, h], L[b, h] = attention_forward(q[b, h], k[b, h], v[b, h], scale, causal=causal)
+    return O, L
+
+
+def _random_qkv(B, H, N, d, dtype, seed, sigma=1.0):
+    return tuple(wl.random_tensor((B, H, N, d), dtype, [seed, t], sigma) for t in (1, 2, 3))
+
+
+# ---------------------------------------------------------------- workloads ---
+
+@pytest.mark.parametrize("cid", [1, 2, 4])
+def test_workload_full_parity(gpu_lib, cid):
+    w = wl.WORKLOADS[cid]
+    q, k, v = wl.make_inputs(w)
+    O, L = run_fwd(gpu_lib, q, k, v, w.dtype)
+    O_ref, L_ref = _oracle_full(q, k, v, w.scale)
+    s = compare(O, L, O_ref, L_ref, w.dtype, w.name)
+    print(f"{w.name}: {s}")
+    if w.kind == "edge":
+        # closed forms on the structured heads
+        for b in range(w.B):
+            for h in range(w.H):
+                cat = wl.edge_category(b, h, w.H)
+                if cat == 0:      # all-zero Q: LSE = ln N, O = column mean of V
+                    np.testing.assert_allclose(L[b, h], np.log(w.N), atol=1e-4)
+                    np.testing.assert_allclose(O[b, h], np.broadcast_to(v[b, h].mean(0), (w.N, w.d)),
+                                               atol=1e-2)
+                elif cat == 2:    # one-hot: O_i = V_{j*(i)} (up to the output rounding)
+                    t = wl.boost_targets(w, b, h)
+                    np.testing.assert_allclose(O[b, h], v[b, h][t], rtol=2 ** -8, atol=1e-6)
+
+
+@pytest.mark.parametrize("cid", [3, 5])
+def test_workload_sampled_rows(gpu_lib, cid):
+    import torch
+
+    w = wl.WORKLOADS[cid]
+    q, k, v = wl.make_inputs(w, threads=16)
+    tq, tk, tv = (to_device(x, w.dtype) for x in (q, k, v))
+    o, lse = gpu_lib.fa_fwd(tq, tk, tv)
+    torch.cuda.synchronize()
+    worst = {}
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = wl.sampled_rows(w, b, h)
+            rr = torch.from_numpy(rows).cuda()
+            Og = to_host(o[b, h].index_select(0, rr))
+            Lg = lse[b, h].index_select(0, rr).cpu().numpy().astype(np.float64)
+            O_ref, L_ref = attention_rows(q[b, h], k[b, h], v[b, h], w.scale, rows)
+            s = compare(Og, Lg, O_ref, L_ref, w.dtype, f"{w.name} b{b} h{h}")
+            worst = {key: max(worst.get(key, 0), val) for key, val in s.items()}
+    # nothing anywhere is NaN/Inf
+    assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
+    print(f"{w.name}: worst over heads {worst}")
+
+
+# ------------------------------------------------------------- ragged tails ---
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 2, 31, 33, 63, 64, 65, 127, 129, 255, 257, 700])
+def test_tail_sweep(gpu_lib, dtype, d, N):
+    q, k, v = _random_qkv(1, 2, N, d, dtype, seed=N * 1000 + d)
+    O, L = run_fwd(gpu_lib, q, k, v, dtype)
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(d))
+    compare(O, L, O_ref, L_ref, dtype, f"N={N} d={d} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 5, 64, 129, 300, 1024])
+def test_causal(gpu_lib, dtype, d, N):
+    q, k, v = _random_qkv(2, 1, N, d, dtype, seed=7 * N + d)
+    O, L = run_fwd(gpu_lib, q, k, v, dtype, causal=True)
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(d), causal=True)
+    compare(O, L, O_ref, L_ref, dtype, f"causal N={N} d={d} {dtype}")
+
+
+# ------------------------------------------------------------ extreme inputs ---
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_large_magnitude_scores(gpu_lib, dtype):
+    # scores of several hundred (fp16 range limits the input scale)
+    sigma = 10.0 if dtype == "bf16" else 4.0
+    q, k, v = _random_qkv(1, 2, 1000, 128, dtype, seed=99, sigma=sigma)
+    v = wl.random_tensor(v.shape, dtype, [99, 9])
+    O, L = run_fwd(gpu_lib, q, k, v, dtype)
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(128))
+    compare(O, L, O_ref, L_ref, dtype, f"x{sigma} {dtype}")
+
+
+def test_custom_scale_and_stream(gpu_lib):
+    import torch
+
+    q, k, v = _random_qkv(2, 3, 333, 64, "bf16", seed=5)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        O, L = run_fwd(gpu_lib, q, k, v, "bf16", scale=0.05, stream=s)
+    O_ref, L_ref = _oracle_full(q, k, v, 0.05)
+    compare(O, L, O_ref, L_ref, "bf16", "scale=0.05 side stream")
+
+
+def test_deterministic_bitwise(gpu_lib):
+    import torch
+
+    q, k, v = _random_qkv(2, 4, 1500, 128, "bf16", seed=3)
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    o1, l1 = gpu_lib.fa_fwd(tq, tk, tv)
+    o2, l2 = gpu_lib.fa_fwd(tq, tk, tv)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+def test_key_value_permutation_invariance(gpu_lib):
+    # Jointly permuting K and V rows leaves the exact result unchanged; the GPU result
+    # changes only by rounding.
+    q, k, v = _random_qkv(1, 2, 777, 128, "bf16", seed=11)
+    perm = np.random.default_rng(0).permutation(777)
+    O1, L1 = run_fwd(gpu_lib, q, k, v, "bf16")
+    O2, L2 = run_fwd(gpu_lib, q, k[:, :, perm], v[:, :, perm], "bf16")
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(128))
+    compare(O1, L1, O_ref, L_ref, "bf16", "original order")
+    compare(O2, L2, O_ref, L_ref, "bf16", "permuted keys")
+
+
+def test_empty_problem_is_a_no_op(gpu_lib):
+    import torch
+
+    z = torch.zeros(2, 3, 0, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = gpu_lib.fa_fwd(z, z, z)
+    assert o.shape == z.shape and lse.shape == (2, 3, 0)
