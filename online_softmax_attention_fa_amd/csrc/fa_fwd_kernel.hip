@@ -69,6 +69,11 @@ template <> struct Elt<__bf16> {
         f32x2 v = {x, y};
         return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
     }
+    // acc + x0 + x1 for a packed pair (v_dot2 against (1, 1))
+    static __device__ __forceinline__ float sum2(unsigned packed, float acc) {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+    }
 };
 template <> struct Elt<_Float16> {
     static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
@@ -78,6 +83,10 @@ template <> struct Elt<_Float16> {
     static __device__ __forceinline__ unsigned pack2(float x, float y) {
         f32x2 v = {x, y};
         return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
+    }
+    static __device__ __forceinline__ float sum2(unsigned packed, float acc) {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
     }
 };
 
@@ -236,9 +245,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int t = 0; t < 16; ++t) o[db][qb][t] = 0.f;
-    float m[QB], lsum[QB];
+    float m[QB], lsum[QB], lrnd[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; lsum[qb] = 0.f; }
+    for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; lsum[qb] = 0.f; lrnd[qb] = 0.f; }
 
     if (n_tiles > 0) {
         load_tile(0);
@@ -317,6 +326,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
                     const float alpha = (m[qb] == -INFINITY) ? 0.f : fast_exp2(m[qb] - mnew);
                     m[qb] = mnew;
                     lsum[qb] *= alpha;
+                    lrnd[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -324,12 +334,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
                 }
             }
 
-            // ---- P = 2^(s*c - m), row sums, pack to the MFMA element type
+            // ---- P = 2^(s*c - m), packed to the MFMA element type.  Two row sums: of
+            // the rounded values (divides O, so the weights applied to V sum exactly to
+            // the divisor) and of the fp32 values (gives LSE).
             u32x4 pf[KS][QB];
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const float neg_m = (m[qb] == -INFINITY) ? 0.f : -m[qb];
-                float acc0 = 0.f, acc1 = 0.f;
+                float acc0 = 0.f, acc1 = 0.f, racc0 = 0.f, racc1 = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     float p[16];
@@ -341,11 +353,16 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
                     for (int half = 0; half < 2; ++half) {
                         u32x4 f;
 #pragma unroll
-                        for (int w = 0; w < 4; ++w) f[w] = Elt<T>::pack2(p[8 * half + 2 * w], p[8 * half + 2 * w + 1]);
+                        for (int w = 0; w < 4; ++w) {
+                            f[w] = Elt<T>::pack2(p[8 * half + 2 * w], p[8 * half + 2 * w + 1]);
+                            if (w & 1) racc1 = Elt<T>::sum2(f[w], racc1);
+                            else racc0 = Elt<T>::sum2(f[w], racc0);
+                        }
                         pf[2 * kb + half][qb] = f;
                     }
                 }
                 lsum[qb] += acc0 + acc1;
+                lrnd[qb] += racc0 + racc1;
             }
 
             // ---- O^T += V_j^T P^T
@@ -374,7 +391,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
         const int row = q_wave + qb * 32 + l32;
         const float lt = pair_sum(lsum[qb]);
-        const float inv = 1.0f / lt;
+        const float inv = 1.0f / pair_sum(lrnd[qb]);
         if (row < N) {
             T* orow = Oh + (int64_t)row * D;
 #pragma unroll
