@@ -110,38 +110,71 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 16-byte chunk swizzle: chunk c of row r is stored at chunk c ^ swz(r).  For any 16
-// consecutive rows read at one logical chunk the physical 16-byte slots differ modulo
-// 256 bytes (and the first 8 modulo 128 bytes).
+// 16-byte chunk swizzle of K and V tiles in LDS (both row-major, RB = 2*D bytes per
+// row): chunk c of row r is stored at chunk c ^ swz(r).  It is chosen so that
+//  * the 16 rows read at one logical chunk by a K-operand ds_read_b128 land in 16
+//    distinct 16-byte slots of a 256-byte bank window, and
+//  * the 4 consecutive rows x 64 bytes read by a V-operand ds_read_b64_tr_b16 lane
+//    group cover the 256-byte window exactly once.
+// D = 128 (16 chunks/row): swap the 2-bit halves of the row's low nibble.
+// D = 64 (8 chunks/row, two rows per window): bit 2 from row bit 1, bits 0-1 from
+// row bits 2-3.
 template <int CPR>
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & (CPR - 1); }
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
-__device__ __forceinline__ u32x4 lds_read16(const unsigned char* p) {
-    return *reinterpret_cast<const u32x4*>(p);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+__device__ __forceinline__ u32x4 lds_read16(const lds_u8* base, int off) {
+    return *reinterpret_cast<const lds_u32x4*>(base + off);
+}
+// Transposing read: see the V operand notes in the kernel.
+__device__ __forceinline__ u32x2 lds_read_tr(const lds_u8* base, int off) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+    return __builtin_bit_cast(u32x2, v);
 }
 
 // ------------------------------------------------------- bf16 / fp16 kernel ---
+//
+// 4 waves x 32 query rows (Br = 128); two workgroups per CU, i.e. two waves per SIMD,
+// so one wave's softmax VALU work overlaps the other's MFMAs.  K/V tiles of BC keys
+// are copied HBM -> LDS with global_load_lds_dwordx4 (no staging registers), two
+// stages, one barrier per tile.  Source rows past N are clamped to row 0 (always a
+// valid, finite row of the same head); their scores are masked to -inf, so they
+// contribute exactly 0.
+//
+// V operand of O^T += V^T P^T: lane L needs V[key][d] for d = 32db + L%32 and the 8
+// keys the P^T accumulator registers of lane L hold.  V stays row-major in LDS and
+// ds_read_b64_tr_b16 gathers it: within each group of 16 lanes, lane c of the group
+// receives element c%4 of the 8-byte pieces addressed by lanes 4e + c/4 (e = 0..3),
+// so if lane r of the group addresses V[k0 + r/4][d0 + 4(r%4) .. +3], lane c gets
+// V[k0 + e][d0 + c] for e = 0..3: four keys of its own column.
 
-template <typename T, int D, int QPW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
-    constexpr int NT = 256, WAVES = 4;
-    constexpr int BR = WAVES * QPW;
-    constexpr int QB = QPW / 32;      // 32-query column blocks per wave
-    constexpr int KB = BC / 32;       // 32-key row blocks per tile
+template <typename T, int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+    constexpr int NT = 256, QPW = 32, BR = 4 * QPW;
+    constexpr int KB = BC / 32;       // 32-key row blocks of S^T per tile
     constexpr int DB = D / 32;        // 32-dim row blocks of O^T
     constexpr int DS = D / 16;        // k-steps of S^T = K Q^T
     constexpr int KS = BC / 16;       // k-steps of O^T += V^T P^T
-    constexpr int CPR_K = D / 8;      // 16-byte chunks per K row
-    constexpr int CPR_V = BC / 8;     // 16-byte chunks per V^T row
-    constexpr int K_BYTES = BC * D * 2;
-    constexpr int V_BYTES = D * BC * 2;
-    constexpr int STAGE = K_BYTES + V_BYTES;
-    constexpr int K_CHUNKS = BC * CPR_K / NT;          // K chunks staged per thread
-    constexpr int V_UNITS = (BC / 4) * (D / 8);        // 4 keys x 8 dims per unit
-    static_assert(K_CHUNKS >= 1 && (BC * CPR_K) % NT == 0, "K staging shape");
-    static_assert(V_UNITS == NT, "V staging: one unit per thread");
+    constexpr int RB = D * 2;         // bytes per K/V row
+    constexpr int CPR = D / 8;        // 16-byte chunks per row
+    constexpr int TILE = BC * RB;     // bytes of one K (or V) tile
+    constexpr int STAGE = 2 * TILE;
+    constexpr int LOADS = TILE / (NT * 16);   // direct loads per thread per tile, K or V
+    static_assert(LOADS >= 1 && TILE % (NT * 16) == 0, "tile must be whole 4 KiB blocks");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+    // Two stages in two separate arrays: the compiler can then prove that the copies
+    // into one stage do not alias the reads of the other and adds no wait for them.
+    __shared__ __attribute__((aligned(1024))) unsigned char stage0_raw[STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char stage1_raw[STAGE];
+    lds_u8* const stage0 = (lds_u8*)stage0_raw;
+    lds_u8* const stage1 = (lds_u8*)stage1_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -159,252 +192,189 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     T* __restrict__ Oh = reinterpret_cast<T*>(a.o) + head;
     float* __restrict__ Lh = a.lse + (int64_t)bh * N;
 
-    const int q_wave = qblk * BR + wave * QPW;     // first query row of this wave
+    const int q_wave = qblk * BR + wave * QPW;   // first query row of this wave
+    const int query = q_wave + l32;              // the query this lane's columns belong to
     const float c = a.c;
 
-    // ---- Q^T fragments (B operand): lane holds query q_wave + qb*32 + l32, dims 16s+8h..+7
-    u32x4 qf[QB][DS];
+    // ---- Q^T fragments (B operand): query row `query`, dims 16s + 8h .. +7
+    u32x4 qf[DS];
+    {
+        const int row = query < N ? query : 0;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = q_wave + qb * 32 + l32;
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row < N) v = *reinterpret_cast<const u32x4*>(Qh + (int64_t)row * D + s * 16 + h * 8);
-            qf[qb][s] = v;
-        }
+        for (int s = 0; s < DS; ++s)
+            qf[s] = *reinterpret_cast<const u32x4*>(Qh + (int64_t)row * D + s * 16 + h * 8);
     }
 
-    // ---- tile range
-    int n_tiles = (int)((N + BC - 1) / BC);
-    if (CAUSAL) {
-        const int q_end = min(N, (qblk + 1) * BR);            // exclusive
-        n_tiles = min(n_tiles, (q_end + BC - 1) / BC);
+    // ---- per-lane LDS offsets (tile and stage offsets are added as immediates)
+    int koff[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) koff[s] = l32 * RB + 16 * ((2 * s + h) ^ swz<CPR>(l32));
+    int voff[2][DB];
+    {
+        const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int key = 8 * aa + 4 * h + (r >> 2);
+                const int dim = 32 * db + 16 * (g & 1) + 4 * (r & 3);
+                voff[aa][db] = TILE + key * RB + 16 * ((dim >> 3) ^ swz<CPR>(key)) + 2 * (dim & 7);
+            }
     }
 
-    // ---- staging registers for the next K/V tile
-    u32x4 kst[K_CHUNKS];
-    u32x4 vst[4];
-    auto load_tile = [&](int j) {
+    // ---- direct HBM -> LDS copy of tile j into a stage (each wave fills 1 KiB blocks)
+    auto issue_tile = [&](int j, lds_u8* stage) {
         const int kbase = j * BC;
 #pragma unroll
-        for (int i = 0; i < K_CHUNKS; ++i) {
-            const int cidx = i * NT + tid;
-            const int row = cidx / CPR_K, ch = cidx % CPR_K;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (kbase + row < N) v = *reinterpret_cast<const u32x4*>(Kh + (int64_t)(kbase + row) * D + ch * 8);
-            kst[i] = v;
-        }
-        const int kg = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = kbase + kg * 4 + r;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (key < N) v = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + dc * 8);
-            vst[r] = v;
-        }
-    };
-    auto store_tile = [&](int stage) {
-        unsigned char* kb_ = smem + stage * STAGE;
-        unsigned char* vb_ = kb_ + K_BYTES;
-#pragma unroll
-        for (int i = 0; i < K_CHUNKS; ++i) {
-            const int cidx = i * NT + tid;
-            const int row = cidx / CPR_K, ch = cidx % CPR_K;
-            *reinterpret_cast<u32x4*>(kb_ + row * (D * 2) + 16 * (ch ^ swz<CPR_K>(row))) = kst[i];
-        }
-        // V^T: this thread holds keys 4kg..4kg+3 x dims 8dc..8dc+7; write, for each dim,
-        // the 4 keys as one 8-byte piece at their permuted position (see header).
-        const int kg = tid / (D / 8), dc = tid % (D / 8);
-        const int k0 = kg * 4;
-        const int g16 = k0 >> 4, kk = k0 & 15;
-        const int pa = kk >> 3, ph = (kk >> 2) & 1;
-        const int chunk = 2 * g16 + ph;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1;
-            unsigned lo, hi;
-            if ((e & 1) == 0) {
-                lo = (vst[0][w] & 0xffffu) | (vst[1][w] << 16);
-                hi = (vst[2][w] & 0xffffu) | (vst[3][w] << 16);
-            } else {
-                lo = (vst[0][w] >> 16) | (vst[1][w] & 0xffff0000u);
-                hi = (vst[2][w] >> 16) | (vst[3][w] & 0xffff0000u);
-            }
-            const int dd = dc * 8 + e;
-            u32x2 piece = {lo, hi};
-            *reinterpret_cast<u32x2*>(vb_ + dd * (BC * 2) + 16 * (chunk ^ swz<CPR_V>(dd)) + 8 * pa) = piece;
+        for (int i = 0; i < LOADS; ++i) {
+            const int off = i * (NT * 16) + wave * 1024 + lane * 16;   // byte offset in the tile
+            const int row = off / RB;
+            const int ch = ((off % RB) >> 4) ^ swz<CPR>(row);
+            int grow = kbase + row;
+            grow = grow < N ? grow : 0;
+            const int64_t src = (int64_t)grow * D + ch * 8;
+            lds_u8* kdst = stage + i * (NT * 16) + wave * 1024;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Kh + src),
+                                             (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Vh + src),
+                                             (__attribute__((address_space(3))) void*)(kdst + TILE), 16, 0, 0);
         }
     };
 
     // ---- running state
-    f32x16 o[DB][QB];
+    f32x16 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int t = 0; t < 16; ++t) o[db][qb][t] = 0.f;
-    float m[QB], lsum[QB], lrnd[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; lsum[qb] = 0.f; lrnd[qb] = 0.f; }
+        for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
+    float m = -INFINITY, lsum = 0.f, lrnd = 0.f;
 
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
-        if (n_tiles > 1) load_tile(1);
-    }
-    __syncthreads();
+    int n_tiles = (N + BC - 1) / BC;
+    if (CAUSAL) n_tiles = min(n_tiles, (min(N, (qblk + 1) * BR) + BC - 1) / BC);
 
-    for (int j = 0; j < n_tiles; ++j) {
+    auto compute_tile = [&](int j, const lds_u8* sbase) {
         const int kbase = j * BC;
-        const unsigned char* kbuf = smem + (j & 1) * STAGE;
-        const unsigned char* vbuf = kbuf + K_BYTES;
+        // ---- S^T = K_j Q^T
+        f32x16 s[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int t = 0; t < 16; ++t) s[kb][t] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                s[kb] = Elt<T>::mma(lds_read16(sbase, koff[ds] + kb * 32 * RB), qf[ds], s[kb]);
 
-        // A wave whose rows all lie before this tile (causal) has nothing to do here.
-        const bool active = !CAUSAL || (kbase <= q_wave + QPW - 1);
-        if (active) {
-            // ---- S^T = K_j Q^T
-            f32x16 s[KB][QB];
+        // ---- masks: keys past N (tail tile), keys after the query (causal)
+        const bool tail = kbase + BC > N;
+        const bool diag = CAUSAL && (kbase + BC - 1 > q_wave);
+        if (tail || diag) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) s[kb][qb][t] = 0.f;
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const int row = kb * 32 + l32;
-                    const u32x4 kf = lds_read16(kbuf + row * (D * 2) + 16 * ((2 * ds + h) ^ swz<CPR_K>(row)));
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = Elt<T>::mma(kf, qf[qb][ds], s[kb][qb]);
+                for (int t = 0; t < 16; ++t) {
+                    const int key = kbase + kb * 32 + 8 * (t >> 2) + 4 * h + (t & 3);
+                    bool drop = key >= N;
+                    if (CAUSAL) drop = drop || key > query;
+                    if (drop) s[kb][t] = -INFINITY;
                 }
-            }
-
-            // ---- masks: keys past N (tail tile), keys after the query (causal)
-            const bool tail = kbase + BC > N;
-            const bool diag = CAUSAL && (kbase + BC - 1 > q_wave);
-            if (tail || diag) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        const int query = q_wave + qb * 32 + l32;
-#pragma unroll
-                        for (int t = 0; t < 16; ++t) {
-                            const int key = kbase + kb * 32 + 8 * (t >> 2) + 4 * h + (t & 3);
-                            bool drop = key >= N;
-                            if (CAUSAL) drop = drop || key > query;
-                            if (drop) s[kb][qb][t] = -INFINITY;
-                        }
-                    }
-            }
-
-            // ---- row maxima of this tile and the (lazy) rescale
-            float mx[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float x0 = -INFINITY, x1 = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int t = 0; t < 16; t += 2) {
-                        x0 = fmaxf(x0, s[kb][qb][t]);
-                        x1 = fmaxf(x1, s[kb][qb][t + 1]);
-                    }
-                mx[qb] = pair_max(fmaxf(x0, x1)) * c;
-            }
-            bool need = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) need = need || (mx[qb] > m[qb] + kRescaleThreshold);
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const float mnew = fmaxf(m[qb], mx[qb]);
-                    const float alpha = (m[qb] == -INFINITY) ? 0.f : fast_exp2(m[qb] - mnew);
-                    m[qb] = mnew;
-                    lsum[qb] *= alpha;
-                    lrnd[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-#pragma unroll
-                        for (int t = 0; t < 16; ++t) o[db][qb][t] *= alpha;
-                }
-            }
-
-            // ---- P = 2^(s*c - m), packed to the MFMA element type.  Two row sums: of
-            // the rounded values (divides O, so the weights applied to V sum exactly to
-            // the divisor) and of the fp32 values (gives LSE).
-            u32x4 pf[KS][QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float neg_m = (m[qb] == -INFINITY) ? 0.f : -m[qb];
-                float acc0 = 0.f, acc1 = 0.f, racc0 = 0.f, racc1 = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    float p[16];
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(s[kb][qb][t], c, neg_m));
-#pragma unroll
-                    for (int t = 0; t < 16; t += 2) { acc0 += p[t]; acc1 += p[t + 1]; }
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        u32x4 f;
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            f[w] = Elt<T>::pack2(p[8 * half + 2 * w], p[8 * half + 2 * w + 1]);
-                            if (w & 1) racc1 = Elt<T>::sum2(f[w], racc1);
-                            else racc0 = Elt<T>::sum2(f[w], racc0);
-                        }
-                        pf[2 * kb + half][qb] = f;
-                    }
-                }
-                lsum[qb] += acc0 + acc1;
-                lrnd[qb] += racc0 + racc1;
-            }
-
-            // ---- O^T += V_j^T P^T
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int dd = db * 32 + l32;
-                    const u32x4 vf = lds_read16(vbuf + dd * (BC * 2) + 16 * ((2 * ks + h) ^ swz<CPR_V>(dd)));
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) o[db][qb] = Elt<T>::mma(vf, pf[ks][qb], o[db][qb]);
-                }
-            }
         }
 
-        // ---- next tile into the other stage; its loads were issued one iteration ago
-        if (j + 1 < n_tiles) {
-            store_tile((j + 1) & 1);
-            if (j + 2 < n_tiles) load_tile(j + 2);
+        // ---- row maximum of the tile (base-2 units) and the lazy rescale
+        float x0 = -INFINITY, x1 = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int t = 0; t < 16; t += 2) {
+                x0 = fmaxf(x0, s[kb][t]);
+                x1 = fmaxf(x1, s[kb][t + 1]);
+            }
+        const float mx = pair_max(fmaxf(x0, x1)) * c;
+        if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold) != 0) {
+            const float mnew = fmaxf(m, mx);
+            const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+            m = mnew;
+            lsum *= alpha;
+            lrnd *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) o[db][t] *= alpha;
         }
+
+        // ---- P = 2^(s*c - m), packed; the O divisor sums the rounded values, LSE the
+        // fp32 ones
+        const float neg_m = (m == -INFINITY) ? 0.f : -m;
+        u32x4 pf[KS];
+        float acc0 = 0.f, acc1 = 0.f, racc0 = 0.f, racc1 = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            float p[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(s[kb][t], c, neg_m));
+#pragma unroll
+            for (int t = 0; t < 16; t += 2) { acc0 += p[t]; acc1 += p[t + 1]; }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                u32x4 f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    f[w] = Elt<T>::pack2(p[8 * half + 2 * w], p[8 * half + 2 * w + 1]);
+                    if (w & 1) racc1 = Elt<T>::sum2(f[w], racc1);
+                    else racc0 = Elt<T>::sum2(f[w], racc0);
+                }
+                pf[2 * kb + half] = f;
+            }
+        }
+        lsum += acc0 + acc1;
+        lrnd += racc0 + racc1;
+
+        // ---- O^T += V_j^T P^T
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x2 lo = lds_read_tr(sbase, voff[0][db] + ks * 16 * RB);
+                const u32x2 hi = lds_read_tr(sbase, voff[1][db] + ks * 16 * RB);
+                const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+                o[db] = Elt<T>::mma(vf, pf[ks], o[db]);
+            }
+    };
+
+    if (n_tiles > 0) issue_tile(0, stage0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's LDS copies have landed
+    __syncthreads();
+
+    for (int j = 0; j < n_tiles; j += 2) {
+        // stage 0 holds tile j; tile j + 1 streams into stage 1 meanwhile
+        if (j + 1 < n_tiles) issue_tile(j + 1, stage1);
+        if (!CAUSAL || j * BC <= q_wave + QPW - 1) compute_tile(j, stage0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (j + 1 >= n_tiles) break;
+        // stage 1 holds tile j + 1
+        if (j + 2 < n_tiles) issue_tile(j + 2, stage0);
+        if (!CAUSAL || (j + 1) * BC <= q_wave + QPW - 1) compute_tile(j + 1, stage1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     }
 
     // ---- epilogue: O / l, LSE = (m + log2 l) ln 2
+    const float lt = pair_sum(lsum);
+    const float inv = 1.0f / pair_sum(lrnd);
+    if (query < N) {
+        T* orow = Oh + (int64_t)query * D;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = q_wave + qb * 32 + l32;
-        const float lt = pair_sum(lsum[qb]);
-        const float inv = 1.0f / pair_sum(lrnd[qb]);
-        if (row < N) {
-            T* orow = Oh + (int64_t)row * D;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    u32x2 w;
-                    w[0] = Elt<T>::pack2(o[db][qb][4 * g + 0] * inv, o[db][qb][4 * g + 1] * inv);
-                    w[1] = Elt<T>::pack2(o[db][qb][4 * g + 2] * inv, o[db][qb][4 * g + 3] * inv);
-                    *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = w;
-                }
-            if (h == 0) Lh[row] = (m[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
-        }
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = Elt<T>::pack2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
+                w[1] = Elt<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+                *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = w;
+            }
+        if (h == 0) Lh[query] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
     }
 }
 
@@ -528,21 +498,21 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
 
 // ------------------------------------------------------------------ dispatch ---
 
-template <typename T, int D, int QPW, int BC>
+template <typename T, int D, int BC>
 static hipError_t launch_t(const FwdArgs& a, int causal, hipStream_t st) {
     const dim3 grid((unsigned)a.n_blocks), block(256);
     if (causal)
-        hipLaunchKernelGGL((fwd_kernel<T, D, QPW, BC, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((fwd_kernel<T, D, BC, true>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((fwd_kernel<T, D, QPW, BC, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((fwd_kernel<T, D, BC, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int causal, hipStream_t st) {
     (void)p;
-    if (d == 128) return launch_t<T, 128, 32, 64>(a, causal, st);
-    return launch_t<T, 64, 32, 128>(a, causal, st);
+    if (d == 128) return launch_t<T, 128, 64>(a, causal, st);
+    return launch_t<T, 64, 128>(a, causal, st);
 }
 
 }  // namespace fa
