@@ -54,6 +54,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309417f;
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
+constexpr int kBufferRsrcWord3 = 0x00020000;
 // Lazy-rescale threshold in base-2 exponent units (P <= 2^8).
 constexpr float kRescaleThreshold = 8.0f;
 
@@ -144,9 +146,8 @@ __device__ __forceinline__ u32x2 lds_read_tr(const lds_u8* base, int off) {
 // 4 waves x 32 query rows (Br = 128); two workgroups per CU, i.e. two waves per SIMD,
 // so one wave's softmax VALU work overlaps the other's MFMAs.  K/V tiles of BC keys
 // are copied HBM -> LDS with global_load_lds_dwordx4 (no staging registers), two
-// stages, one barrier per tile.  Source rows past N are clamped to row 0 (always a
-// valid, finite row of the same head); their scores are masked to -inf, so they
-// contribute exactly 0.
+// stages, one barrier per tile.  Rows past N read as zeros (buffer range check) and
+// their scores are masked to -inf, so they contribute exactly 0.
 //
 // V operand of O^T += V^T P^T: lane L needs V[key][d] for d = 32db + L%32 and the 8
 // keys the P^T accumulator registers of lane L hold.  V stays row-major in LDS and
@@ -157,6 +158,7 @@ __device__ __forceinline__ u32x2 lds_read_tr(const lds_u8* base, int off) {
 
 template <typename T, int D, int BC, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource types exist only in the device pass
     constexpr int NT = 256, QPW = 32, BR = 4 * QPW;
     constexpr int KB = BC / 32;       // 32-key row blocks of S^T per tile
     constexpr int DB = D / 32;        // 32-dim row blocks of O^T
@@ -177,7 +179,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     lds_u8* const stage1 = (lds_u8*)stage1_raw;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
     const int h = lane >> 5, l32 = lane & 31;
     const int N = a.n;
 
@@ -222,22 +225,32 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             }
     }
 
-    // ---- direct HBM -> LDS copy of tile j into a stage (each wave fills 1 KiB blocks)
+    // ---- direct HBM -> LDS copy of tile j into a stage, through buffer resources that
+    // cover exactly this head's K (V): reads past row N - 1 return zeros, so the ragged
+    // last tile needs no special case (its padded keys are also masked to -inf).
+    // Wave w, copy i fills the 1 KiB block i*4 + w of the tile; lane L's 16 bytes land
+    // at block + 16 L, i.e. row `row`, swizzled chunk `ch`.  The per-lane byte offset is
+    // loop invariant; the tile offset is the scalar soffset.
+    const int head_bytes = N * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, head_bytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, head_bytes, kBufferRsrcWord3);
+    int src_off[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int off = i * (NT * 16) + wave * 1024 + lane * 16;   // byte offset in the tile
+        const int row = off / RB;
+        const int ch = ((off % RB) >> 4) ^ swz<CPR>(row);
+        src_off[i] = row * RB + ch * 16;
+    }
     auto issue_tile = [&](int j, lds_u8* stage) {
-        const int kbase = j * BC;
+        const int soff = j * BC * RB;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int off = i * (NT * 16) + wave * 1024 + lane * 16;   // byte offset in the tile
-            const int row = off / RB;
-            const int ch = ((off % RB) >> 4) ^ swz<CPR>(row);
-            int grow = kbase + row;
-            grow = grow < N ? grow : 0;
-            const int64_t src = (int64_t)grow * D + ch * 8;
             lds_u8* kdst = stage + i * (NT * 16) + wave * 1024;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Kh + src),
-                                             (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Vh + src),
-                                             (__attribute__((address_space(3))) void*)(kdst + TILE), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16,
+                                                     src_off[i], soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(kdst + TILE), 16,
+                                                     src_off[i], soff, 0, 0);
         }
     };
 
@@ -260,11 +273,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int t = 0; t < 16; ++t) s[kb][t] = 0.f;
+        // K fragments are read one k-step ahead of the MFMAs that use them
+        u32x4 kf[2][KB];
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
+        for (int kb = 0; kb < KB; ++kb) kf[0][kb] = lds_read16(sbase, koff[0] + kb * 32 * RB);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                s[kb] = Elt<T>::mma(lds_read16(sbase, koff[ds] + kb * 32 * RB), qf[ds], s[kb]);
+        for (int ds = 0; ds < DS; ++ds) {
+            if (ds + 1 < DS) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) kf[(ds + 1) & 1][kb] = lds_read16(sbase, koff[ds + 1] + kb * 32 * RB);
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) s[kb] = Elt<T>::mma(kf[ds & 1][kb], qf[ds], s[kb]);
+        }
 
         // ---- masks: keys past N (tail tile), keys after the query (causal)
         const bool tail = kbase + BC > N;
@@ -376,6 +397,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             }
         if (h == 0) Lh[query] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
     }
+#endif
 }
 
 // ------------------------------------------------------------- fp32 kernel ---
