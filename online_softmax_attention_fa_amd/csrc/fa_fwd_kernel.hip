@@ -267,6 +267,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
     auto compute_tile = [&](int j, const lds_u8* sbase) {
         const int kbase = j * BC;
+        // MFMA-heavy stretches run at raised wave priority, so the SIMD issues them
+        // ahead of the other wave's VALU work
+        __builtin_amdgcn_s_setprio(1);
         // ---- S^T = K_j Q^T
         f32x16 s[KB];
 #pragma unroll
@@ -287,6 +290,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             for (int kb = 0; kb < KB; ++kb) s[kb] = Elt<T>::mma(kf[ds & 1][kb], qf[ds], s[kb]);
         }
 
+        __builtin_amdgcn_s_setprio(0);
         // ---- masks: keys past N (tail tile), keys after the query (causal)
         const bool tail = kbase + BC > N;
         const bool diag = CAUSAL && (kbase + BC - 1 > q_wave);
@@ -352,6 +356,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         lrnd += racc0 + racc1;
 
         // ---- O^T += V_j^T P^T
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -361,6 +366,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
                 o[db] = Elt<T>::mma(vf, pf[ks], o[db]);
             }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     if (n_tiles > 0) issue_tile(0, stage0);
