@@ -105,6 +105,36 @@ fa_status fa_fwd_causal(const void* Q, const void* K, const void* V, void* O, fl
 fa_status fa_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype,
                       int causal, fa_plan* plan);
 
+/*
+ * Workspace the backward needs, in bytes: two fp32 values per row (B*H*N rows).
+ * Returns 0 for invalid or empty shapes.
+ */
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype);
+
+/*
+ * Recompute-based backward of fa_fwd ("从原理出发理解 Flash Attention Part2", section
+ * 2.4; "从零理解Flash Attention中的online softmax", section 5.1): P is rebuilt from the
+ * saved LSE, never stored.  With D_i = sum_k dO_ik O_ik:
+ *     dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ * Inputs: Q, K, V, O, dO [B,H,N,d] of `dtype`; LSE [B,H,N] fp32 exactly as fa_fwd wrote
+ * them.  Outputs dQ, dK, dV [B,H,N,d] of `dtype` (overwritten, not accumulated).
+ * `workspace` is device memory of at least fa_bwd_workspace_bytes(...) bytes, 256-byte
+ * aligned, owned by the caller; its contents on entry are ignored.  Supported: dtype
+ * FA_BF16 / FA_F16, d in {64, 128} (FA_F32 returns FA_ERR_UNSUPPORTED).  Deterministic
+ * (no atomics).  Validation as fa_fwd, plus FA_ERR_WORKSPACE for a NULL, misaligned or
+ * short workspace.
+ */
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                 const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t ws_bytes,
+                 int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
+                 void* stream);
+
+/* Backward of fa_fwd_causal (keys after the query row get P = 0). */
+fa_status fa_bwd_causal(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                        const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t ws_bytes,
+                        int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
+                        void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(fa_status s);
 

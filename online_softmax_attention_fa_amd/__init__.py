@@ -24,7 +24,8 @@ STATUS = {
 }
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_causal", "fa_fwd_plan", "fa_status_str", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_causal", "fa_fwd_plan", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal",
+           "fa_status_str", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -63,6 +64,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).restype = I
     lib.fa_fwd_plan.argtypes = [I64, I64, I64, I64, I, I, ctypes.POINTER(Plan)]
     lib.fa_fwd_plan.restype = I
+    lib.fa_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    bwd_args = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, I64, I64, I64, I64, F, I, P]
+    for name in ("fa_bwd", "fa_bwd_causal"):
+        getattr(lib, name).argtypes = bwd_args
+        getattr(lib, name).restype = I
     lib.fa_status_str.argtypes = [I]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -146,6 +153,56 @@ def fa_fwd(q, k, v, o=None, lse=None, scale=None, stream=None, causal=False):
 
 def fa_fwd_causal(q, k, v, o=None, lse=None, scale=None, stream=None):
     return fa_fwd(q, k, v, o=o, lse=lse, scale=scale, stream=stream, causal=True)
+
+
+def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
+    """Bytes of device workspace ``fa_bwd`` needs (0 for an invalid or empty shape)."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(load().fa_bwd_workspace_bytes(B, H, N, d, code))
+
+
+def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None, scale=None,
+           stream=None, causal=False):
+    """dQ, dK, dV of attention through ``fa_bwd`` (or ``fa_bwd_causal``).
+
+    q, k, v, o, do: contiguous device tensors [B, H, N, d] (fp16 / bf16); lse: fp32
+    [B, H, N] from the forward with the same scale and masking.  dq, dk, dv: optional
+    preallocated outputs; workspace: optional uint8 device tensor of at least
+    ``fa_bwd_workspace_bytes`` bytes.  Returns (dq, dk, dv).
+    """
+    import torch
+
+    lib = load()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    for name, t in (("o", o), ("do", do)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous device tensor shaped and typed like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous, shaped and typed like q")
+    code = dtype_code(q.dtype)
+    need = int(lib.fa_bwd_workspace_bytes(B, H, N, d, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    fn = lib.fa_bwd_causal if causal else lib.fa_bwd
+    with torch.cuda.device(q.device):
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                B, H, N, d, float(scale), code, _stream_handle(stream))
+    _check(st, "fa_bwd_causal" if causal else "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_bwd_causal(q, k, v, o, lse, do, **kw):
+    return fa_bwd(q, k, v, o, lse, do, causal=True, **kw)
 
 
 def fa_fwd_plan(B, H, N, d, dtype, causal=False) -> dict:

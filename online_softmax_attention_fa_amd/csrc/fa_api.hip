@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 constexpr int kMaxDevices = 64;
 
 struct DeviceInfo {
@@ -81,9 +81,67 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
     return e == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 
+fa_status bwd_common(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* LSE, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
+                     void* stream, int causal) {
+    fa_status st = check_problem(B, H, N, d, dtype);
+    if (st != FA_OK) return st;
+    if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+    if (B * H * N == 0) return FA_OK;
+    if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
+        !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(LSE, 4))
+        return FA_ERR_ALIGN;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+    if (!ws || !aligned(ws, 256) || ws_bytes < fa::bwd_workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+    st = check_device();
+    if (st != FA_OK) return st;
+
+    const size_t one = fa::bwd_workspace_bytes(B, H, N) / 2;
+    fa::BwdArgs a;
+    a.q = Q;
+    a.k = K;
+    a.v = V;
+    a.o = O;
+    a.dout = dO;
+    a.lse = LSE;
+    a.dq = dQ;
+    a.dk = dK;
+    a.dv = dV;
+    a.dsum = reinterpret_cast<float*>(ws);
+    a.l2 = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) + one);
+    a.n = (int)N;
+    a.n_blk = 0;
+    a.n_blocks = 0;
+    a.c = (float)((double)scale * 1.4426950408889634074);
+    a.scale = scale;
+    const int e = fa_launch_bwd(a, B * H * N, dtype, (int)d, causal, stream);
+    return e == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype) {
+    if (check_problem(B, H, N, d, dtype) != FA_OK) return 0;
+    return fa::bwd_workspace_bytes(B, H, N);
+}
+
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                 const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t ws_bytes,
+                 int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype, void* stream) {
+    return bwd_common(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, ws_bytes, B, H, N, d, scale, dtype, stream, 0);
+}
+
+fa_status fa_bwd_causal(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                        const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t ws_bytes,
+                        int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
+                        void* stream) {
+    return bwd_common(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, ws_bytes, B, H, N, d, scale, dtype, stream, 1);
+}
+
 
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,

@@ -5,6 +5,7 @@
 // check it.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/fa.h"
@@ -23,6 +24,32 @@ struct FwdArgs {
     int n_blocks;   // workgroups in the grid = B*H*n_qblk
     float c;        // scale * log2(e): scores are taken to base 2 inside the kernel
 };
+
+// Kernel arguments of the backward pass.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dsum;    // workspace: D = rowsum(dO * O), [B, H, N]
+    float* l2;      // workspace: LSE * log2(e), [B, H, N]
+    int n;
+    int n_blk;      // 128-row blocks per head (query blocks for dQ, key blocks for dK/dV)
+    int n_blocks;
+    float c;        // scale * log2(e)
+    float scale;
+};
+
+// Workspace of the backward: two fp32 values per row, each array 256-byte aligned.
+inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+    const size_t one = (size_t)(B * H * N) * sizeof(float);
+    return 2 * ((one + 255) / 256 * 256);
+}
 
 // Kernel variants compiled into the library.  kind: 0 = fp32, 1 = fp16, 2 = bf16.
 struct FwdVariant {
@@ -81,3 +108,5 @@ inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int d
 // hipError_t of the launch.
 int fa_launch_fwd(const fa::FwdArgs& a, const fa_plan& plan, int dtype, int d, int causal,
                   void* stream);
+// rows = B*H*N.  Launches the preprocess, dQ and dK/dV kernels in stream order.
+int fa_launch_bwd(const fa::BwdArgs& a, int64_t rows, int dtype, int d, int causal, void* stream);

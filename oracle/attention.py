@@ -240,9 +240,10 @@ def attention_backward(Q, K, V, dO, scale, causal=False, return_all=False):
     return dQ, dK, dV
 
 
-def backward_rows_dq(Q, K, V, dO, scale, rows, causal=False):
+def backward_rows_dq(Q, K, V, dO, scale, rows, causal=False, return_all=False):
     """dQ for selected query rows of one head ([N, d] inputs); each dQ row needs only its own
-    query row, dO row and all of K, V (same formulas as :func:`attention_backward`)."""
+    query row, dO row and all of K, V (same formulas as :func:`attention_backward`).
+    With ``return_all`` also returns the rows' P, dS, O and D."""
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
     rows = np.asarray(rows)
     S = scale * (Q[rows] @ K.T)
@@ -255,6 +256,8 @@ def backward_rows_dq(Q, K, V, dO, scale, rows, causal=False):
     dP = dO[rows] @ V.T
     D = (dO[rows] * O).sum(axis=-1, keepdims=True)
     dS = P * (dP - D)
+    if return_all:
+        return scale * (dS @ K), dict(P=P, dS=dS, O=O, D=D[:, 0])
     return scale * (dS @ K)
 
 

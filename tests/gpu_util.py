@@ -78,3 +78,73 @@ def run_fwd(fa, q, k, v, dtype, causal=False, scale=None, stream=None):
 
 def scale_of(d):
     return 1.0 / math.sqrt(d)
+
+
+# Gradients.  The backward rebuilds P in fp32, rounds P and dS = P * (dP - D) to the
+# input type before the second products, and forms D from O as stored (rounded, and
+# carrying the forward's own error, whose size is that of rounding P).  With u the unit
+# roundoff of the input type (2^-8 bf16, 2^-11 fp16), first-order error analysis gives,
+# elementwise,
+#     |d dV| <= u (P^T |dO|),
+#     |d dK| <= u scale (|dS|^T |Q| + (P * E)^T |Q|),
+#     |d dQ| <= u scale (|dS| |K| + E * (P |K|)),
+# with E_i = 2 sum_k |dO_ik| (P |V|)_ik bounding the error of D_i.  Values that round into
+# the subnormal range carry an absolute error of up to eta (half the smallest subnormal
+# spacing: 2^-25 fp16, 2^-134 bf16) instead, adding eta times the other operand's absolute
+# column sums.  The test allows twice these (fp32 accumulation and exp2 rounding are
+# second order) plus half an output ulp, and separately bounds the normwise relative
+# error.
+UNIT_ROUNDOFF = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
+SUBNORMAL_HALF_STEP = {"fp16": 2.0 ** -25, "bf16": 2.0 ** -134}
+GRAD_REL_FRO = {"fp16": 2e-3, "bf16": 1e-2}
+
+
+def _d_error_weight(V, dO, P):
+    """E_i = 2 sum_k |dO_ik| (P |V|)_ik: bound on the error of D_i (O rounded and carrying
+    the forward's error)."""
+    return 2.0 * (np.abs(dO) * (P @ np.abs(V))).sum(axis=-1)
+
+
+def mass_dq(K, V, dO, scale, P, dS, dtype):
+    """Error mass of dQ for query rows r: P, dS [r, N]; dO [r, d]; K, V all keys."""
+    E = _d_error_weight(V, dO, P)
+    aK = np.abs(K)
+    floor = SUBNORMAL_HALF_STEP[dtype] / UNIT_ROUNDOFF[dtype] * aK.sum(axis=0)
+    return scale * (np.abs(dS) @ aK + E[:, None] * (P @ aK) + floor[None, :])
+
+
+def mass_dkdv(Q, V, dO, scale, P, dS, dtype, cols=None):
+    """Error masses of dK, dV for key columns ``cols`` (all if None), summed over the query
+    rows r given: P, dS [r, N]; Q, dO [r, d].  Row blocks add up."""
+    E = _d_error_weight(V, dO, P)
+    if cols is not None:
+        P, dS = P[:, cols], dS[:, cols]
+    aQ, adO = np.abs(Q), np.abs(dO)
+    f = SUBNORMAL_HALF_STEP[dtype] / UNIT_ROUNDOFF[dtype]
+    m_dk = scale * (np.abs(dS).T @ aQ + (P * E[:, None]).T @ aQ + f * aQ.sum(axis=0)[None, :])
+    m_dv = P.T @ adO + f * adO.sum(axis=0)[None, :]
+    return m_dk, m_dv
+
+
+def compare_grad(G, G_ref, dtype: str, what: str = "", mass=None, check_fro: bool = True):
+    """Pass iff |G - G_ref| <= 2 u mass + half an output ulp elementwise, the relative
+    Frobenius error is within GRAD_REL_FRO (unless ``check_fro`` is off: there the
+    gradient is a small difference of large terms and only the elementwise bound, which
+    accounts for that, is asserted), and nothing is NaN/Inf."""
+    assert np.all(np.isfinite(G)), f"{what}: non-finite gradient"
+    err = np.abs(G - G_ref)
+    bound = 2.0 * UNIT_ROUNDOFF[dtype] * mass + half_ulp(G_ref, dtype)
+    bad = err > bound
+    den = np.linalg.norm(G_ref)
+    rel = float(np.linalg.norm(G - G_ref) / den) if den > 0 else float(np.linalg.norm(G))
+    ratio = err / bound
+    summary = dict(max_err=float(err.max()) if err.size else 0.0, rel_fro=rel,
+                   max_err_over_bound=float(ratio.max()) if ratio.size else 0.0,
+                   max_ref=float(np.abs(G_ref).max()) if G_ref.size else 0.0)
+    if bad.any():
+        idx = np.unravel_index(np.argmax(ratio), err.shape)
+        raise AssertionError(f"{what}: error {err[idx]:.3e} > bound {bound[idx]:.3e} at {idx} "
+                             f"(got {G[idx]}, ref {G_ref[idx]}); {int(bad.sum())} elements out; {summary}")
+    if check_fro:
+        assert rel <= GRAD_REL_FRO[dtype], f"{what}: relative Frobenius error {rel:.3e}; {summary}"
+    return summary

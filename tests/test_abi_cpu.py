@@ -102,6 +102,56 @@ def test_valid_call_without_gpu_stops_at_device_check(lib):
     assert _fwd(lib, causal=True) == 6
 
 
+WS = 0x20000  # 256-byte aligned fake workspace
+
+
+def _bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=WS,
+         ws_bytes=None, B=1, H=2, N=64, d=64, scale=0.125, dtype=fa.FA_BF16, causal=False):
+    if ws_bytes is None:
+        ws_bytes = 2 * 4 * B * H * N + 512
+    fn = lib.fa_bwd_causal if causal else lib.fa_bwd
+    return fn(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, N, d, scale, dtype, None)
+
+
+def test_bwd_workspace_size(lib):
+    # two fp32 arrays of B*H*N, each rounded up to 256 bytes
+    assert lib.fa_bwd_workspace_bytes(1, 1, 64, 64, fa.FA_BF16) == 512
+    assert lib.fa_bwd_workspace_bytes(1, 1, 65, 64, fa.FA_BF16) == 1024
+    assert lib.fa_bwd_workspace_bytes(4, 32, 16384, 128, fa.FA_BF16) == 2 * 4 * 4 * 32 * 16384
+    assert lib.fa_bwd_workspace_bytes(1, 1, 64, 80, fa.FA_BF16) == 0
+    assert lib.fa_bwd_workspace_bytes(1, -1, 64, 64, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_bytes(2, 8, 4097, 128, fa.FA_F16) == 2 * (-(-2 * 8 * 4097 * 4 // 256) * 256)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_validation_order_and_codes(lib, causal):
+    assert _bwd(lib, q=None, causal=causal) == 1
+    assert _bwd(lib, dv=None, causal=causal) == 1
+    assert _bwd(lib, do=None, N=-1, causal=causal) == 2
+    assert _bwd(lib, d=96, causal=causal) == 3
+    assert _bwd(lib, dtype=fa.FA_F32, causal=causal) == 3     # backward: 16-bit inputs only
+    assert _bwd(lib, q=None, N=0, causal=causal) == 0         # empty: NULLs allowed
+    assert _bwd(lib, ws=None, N=0, causal=causal) == 0
+    assert _bwd(lib, dk=FAKE + 8, causal=causal) == 4
+    assert _bwd(lib, do=FAKE + 2, causal=causal) == 4
+    assert _bwd(lib, lse=FAKE + 2, causal=causal) == 4
+    assert _bwd(lib, scale=0.0, causal=causal) == 5
+    assert _bwd(lib, scale=float("nan"), causal=causal) == 5
+    assert _bwd(lib, ws=None, causal=causal) == 8
+    assert _bwd(lib, ws=WS + 16, causal=causal) == 8          # 256-byte alignment
+    assert _bwd(lib, ws_bytes=511, causal=causal) == 8
+    assert _bwd(lib, N=1 << 25, d=128, causal=causal) == 2
+
+
+def test_bwd_valid_call_without_gpu_stops_at_device_check(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; the device check passes")
+    assert _bwd(lib) == 6
+    assert _bwd(lib, causal=True, dtype=fa.FA_F16, d=128) == 6
+
+
 @pytest.mark.parametrize("dtype", [fa.FA_F32, fa.FA_F16, fa.FA_BF16])
 @pytest.mark.parametrize("d", [64, 128])
 def test_plan_respects_lds_and_covers_rows(lib, dtype, d):
@@ -136,4 +186,5 @@ def test_library_has_no_torch_dependency():
     import subprocess
 
     out = subprocess.run(["ldd", fa.LIB_PATH], capture_output=True, text=True).stdout
-    assert "torch" not in out and "c10" not in out
+    names = [line.split()[0] for line in out.splitlines() if line.strip()]   # not the load addresses
+    assert names and not any("torch" in n or n.startswith("libc10") for n in names), names
