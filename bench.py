@@ -1,7 +1,7 @@
 """Benchmark of the fused attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--copy-calibration BYTES]
+                    [--no-backward] [--copy-calibration BYTES]
 
 Workload: B=4, H=32, N=16384, d=128, bf16 Q/K/V, scale 1/sqrt(d), non-causal, one
 forward per step through the C ABI (fa_fwd) with inputs resident in HBM.  Prints
@@ -13,6 +13,9 @@ ONE JSON line on stdout (everything else goes to stderr):
              events on the launch stream; `traffic` is HBM bytes per launch from the
              committed rocprofv3 counter summary when it was taken on the current
              kernel source, else null
+  backward   the recompute-based backward (fa_bwd) on the same tensors with seeded dO,
+             timed separately after the forward; TFLOP/s counted as 10*B*H*N^2*d
+             (2.5x the forward: S, dP, dV, dK, dQ), not part of `value`
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload (whole heads
              in row chunks, all keys, about 15 s of host time), timed on the host
              cores, with the GPU output checked on the same rows
@@ -36,6 +39,7 @@ METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) and % of MI355X bf16 MFMA peak
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 B, H, N, D = 4, 32, 16384, 128
 KERNEL_SOURCES = ("online_softmax_attention_fa_amd/csrc/fa_fwd_kernel.hip",
+                  "online_softmax_attention_fa_amd/csrc/fa_device.h",
                   "online_softmax_attention_fa_amd/csrc/fa_internal.h")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fa_fwd_bf16_B4_H32_N16384_d128_counters.md")
 
@@ -119,12 +123,41 @@ def cpu_baseline(q, k, v, o, lse, scale, budget_s=15.0, chunk=2048):
     }
 
 
+def time_backward(fa, q, k, v, o, lse, scale, stream, steps):
+    """fa_bwd on the forward's O and LSE with seeded dO; events on the launch stream."""
+    import torch
+
+    gen = torch.Generator(device=q.device).manual_seed(20240602)
+    do = torch.randn(q.shape, device=q.device, dtype=q.dtype, generator=gen)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, D, q.dtype), dtype=torch.uint8, device=q.device)
+    fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale=scale, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale=scale, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    flops = 10.0 * B * H * N * N * D
+    tflops = flops / (ms * 1e-3) / 1e12
+    ok = all(torch.isfinite(t).all().item() for t in (dq, dk, dv))
+    log(f"backward {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (10*B*H*N^2*d), finite={ok}")
+    return {"ms_per_step": round(ms, 4), "tflops": round(tflops, 2), "steps": steps,
+            "flops_per_step": flops, "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+            "outputs_finite": ok}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -214,6 +247,8 @@ def main():
             "traffic": traffic,
         },
     }
+    if not args.no_backward:
+        out["backward"] = time_backward(fa, q, k, v, o, lse, scale, stream, args.backward_steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, o, lse, scale)
     print(json.dumps(out), flush=True)

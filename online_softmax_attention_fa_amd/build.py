@@ -35,6 +35,10 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source extra hipcc flags, by file name (none at present).
+FILE_FLAGS = {}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -49,7 +53,7 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
+def build(verbose: bool = False, extra_flags=None, out: str = LIB) -> str:
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     flags = COMMON_FLAGS + list(extra_flags or [])
@@ -58,18 +62,19 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         srcs = sources()
         objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
         with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-            outs = list(ex.map(lambda so: _run([HIPCC, *flags, "-c", so[0], "-o", so[1]]),
+            outs = list(ex.map(lambda so: _run([HIPCC, *flags, *FILE_FLAGS.get(os.path.basename(so[0]), []),
+                                                "-c", so[0], "-o", so[1]]),
                                zip(srcs, objs)))
         if verbose:
             for o in outs:
                 if o.strip():
                     print(o)
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = out + ".tmp"
         _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib])
-        os.replace(tmp_lib, LIB)
+        os.replace(tmp_lib, out)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

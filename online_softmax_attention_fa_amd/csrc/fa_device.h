@@ -76,6 +76,12 @@ __device__ __forceinline__ int remap_xcd(int bid, int n) {
     return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// max(a, b, c) with NaN propagation: lowers to one v_maximum3_f32 and, unlike fmaxf,
+// needs no canonicalisation of MFMA results first.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+}
+
 // Value of x in lane L^32 combined with x: returns {x[L%32], x[L%32 + 32]} in some order.
 __device__ __forceinline__ float pair_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

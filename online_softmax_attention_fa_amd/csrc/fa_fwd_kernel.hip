@@ -210,11 +210,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int t = 0; t < 16; t += 2) {
-                x0 = fmaxf(x0, s[kb][t]);
-                x1 = fmaxf(x1, s[kb][t + 1]);
+            for (int t = 0; t < 16; t += 4) {
+                x0 = vmax3(x0, s[kb][t], s[kb][t + 1]);
+                x1 = vmax3(x1, s[kb][t + 2], s[kb][t + 3]);
             }
-        const float mx = pair_max(fmaxf(x0, x1)) * c;
+        const float mx = pair_max(__builtin_elementwise_maximum(x0, x1)) * c;
         if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold) != 0) {
             const float mnew = fmaxf(m, mx);
             const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);

@@ -79,10 +79,10 @@ inline int fwd_lds_bytes(int dtype, int d, int block_k) {
 
 // The chooser.  Inputs are already validated (d in {64,128}, dtype known, N > 0).
 //
-// bf16/fp16: 4 waves per workgroup, one wave per SIMD, 32 query rows per wave
-// (one 32-row MFMA column block), Br = 128.  Bc = 64 keys per LDS stage at
-// d = 128 and 128 at d = 64 (so a K or V stage is 16 KiB either way; 64 KiB with
-// double buffering, well inside the 160 KiB of a CU).
+// bf16/fp16: 4 waves per workgroup, 32 query rows per wave (one 32-row MFMA column
+// block), Br = 128, two workgroups (two waves per SIMD) per CU.  Bc = 64 keys per LDS
+// stage at d = 128 and 128 at d = 64, so a K or V stage is 16 KiB either way; the two
+// stages take 64 KiB of the 160 KiB of a CU.
 // fp32: 4 waves x 32 rows, Bc = 32, single-stage LDS (latency-bound sizes only).
 inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal) {
     fa_plan p{};
