@@ -25,8 +25,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 constexpr float kLn2 = 0.693147180559945309417f;
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle).
 constexpr int kBufferRsrcWord3 = 0x00020000;
-// Lazy-rescale threshold in base-2 exponent units (P <= 2^8).
-constexpr float kRescaleThreshold = 8.0f;
+// Largest per-lane sum of one tile's P accepted before the tile is redone with its own
+// row maximum: keeps every P below 2^15, inside the fp16 range.
+constexpr float kMaxTileSum = 32768.0f;
 
 // ------------------------------------------------------------------ helpers ---
 

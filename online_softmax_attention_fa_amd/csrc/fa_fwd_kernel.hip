@@ -205,17 +205,47 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 }
         }
 
-        // ---- row maximum of the tile (base-2 units) and the lazy rescale
-        float x0 = -INFINITY, x1 = -INFINITY;
+        // ---- P = 2^(s*c - m), packed; the O divisor sums the rounded values, LSE the fp32
+        // ones.  P is first formed with the running maximum m as it stands: the exact softmax
+        // does not depend on m, which only has to keep P finite and in range.  A tile is
+        // redone with its own maximum when some row's tile sum leaves [0, 2^15] -- the first
+        // tile (m = -inf), or a row maximum that jumped by more than 15 in base-2 units.
+        u32x4 pf[KS];
+        float acc0, acc1, racc0, racc1;
+        auto make_p = [&](float neg_m) {
+            acc0 = 0.f, acc1 = 0.f, racc0 = 0.f, racc1 = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb) {
+                float p[16];
 #pragma unroll
-            for (int t = 0; t < 16; t += 4) {
-                x0 = vmax3(x0, s[kb][t], s[kb][t + 1]);
-                x1 = vmax3(x1, s[kb][t + 2], s[kb][t + 3]);
+                for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(s[kb][t], c, neg_m));
+#pragma unroll
+                for (int t = 0; t < 16; t += 2) { acc0 += p[t]; acc1 += p[t + 1]; }
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    u32x4 f;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        f[w] = Elt<T>::pack2(p[8 * half + 2 * w], p[8 * half + 2 * w + 1]);
+                        if (w & 1) racc1 = Elt<T>::sum2(f[w], racc1);
+                        else racc0 = Elt<T>::sum2(f[w], racc0);
+                    }
+                    pf[2 * kb + half] = f;
+                }
             }
-        const float mx = pair_max(__builtin_elementwise_maximum(x0, x1)) * c;
-        if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold) != 0) {
+        };
+        make_p(-m);
+        // (NaN, from -inf scores against m = -inf, also fails the test)
+        if (__builtin_amdgcn_ballot_w64(!(acc0 + acc1 <= kMaxTileSum)) != 0) {
+            float x0 = -INFINITY, x1 = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int t = 0; t < 16; t += 4) {
+                    x0 = vmax3(x0, s[kb][t], s[kb][t + 1]);
+                    x1 = vmax3(x1, s[kb][t + 2], s[kb][t + 3]);
+                }
+            const float mx = pair_max(__builtin_elementwise_maximum(x0, x1)) * c;
             const float mnew = fmaxf(m, mx);
             const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
             m = mnew;
@@ -225,31 +255,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int t = 0; t < 16; ++t) o[db][t] *= alpha;
-        }
-
-        // ---- P = 2^(s*c - m), packed; the O divisor sums the rounded values, LSE the
-        // fp32 ones
-        const float neg_m = (m == -INFINITY) ? 0.f : -m;
-        u32x4 pf[KS];
-        float acc0 = 0.f, acc1 = 0.f, racc0 = 0.f, racc1 = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            float p[16];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(s[kb][t], c, neg_m));
-#pragma unroll
-            for (int t = 0; t < 16; t += 2) { acc0 += p[t]; acc1 += p[t + 1]; }
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                u32x4 f;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    f[w] = Elt<T>::pack2(p[8 * half + 2 * w], p[8 * half + 2 * w + 1]);
-                    if (w & 1) racc1 = Elt<T>::sum2(f[w], racc1);
-                    else racc0 = Elt<T>::sum2(f[w], racc0);
-                }
-                pf[2 * kb + half] = f;
-            }
+            make_p(-m);
         }
         lsum += acc0 + acc1;
         lrnd += racc0 + racc1;
@@ -385,7 +391,8 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) x = fmaxf(x, s[t]);
         const float mx = pair_max(x) * c;
-        if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold) != 0) {
+        // lazy rescale: the maximum moves only when a tile exceeds it by 2^8 (P <= 256)
+        if (__builtin_amdgcn_ballot_w64(mx > m + 8.0f) != 0) {
             const float mnew = fmaxf(m, mx);
             const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
             m = mnew;
