@@ -41,10 +41,11 @@ namespace fa {
 
 // ------------------------------------------------------- bf16 / fp16 kernel ---
 //
-// 4 waves x 32 query rows (Br = 128); two workgroups per CU, i.e. two waves per SIMD,
-// so one wave's softmax VALU work overlaps the other's MFMAs.  K/V tiles of BC keys
-// are copied HBM -> LDS with global_load_lds_dwordx4 (no staging registers), two
-// stages, one barrier per tile.  Rows past N read as zeros (buffer range check) and
+// WAVES waves x 32 query rows (Br = 32 WAVES): 4 waves and two workgroups per CU, or
+// 8 waves and one workgroup per CU -- two waves per SIMD either way, so one wave's
+// softmax VALU work overlaps the other's MFMAs.  K/V tiles of BC keys are copied
+// HBM -> LDS with buffer_load_dwordx4 ... lds (no staging registers), two stages, one
+// barrier per tile.  Rows past N read as zeros (buffer range check) and
 // their scores are masked to -inf, so they contribute exactly 0.
 //
 // V operand of O^T += V^T P^T: lane L needs V[key][d] for d = 32db + L%32 and the 8
@@ -54,10 +55,10 @@ namespace fa {
 // so if lane r of the group addresses V[k0 + r/4][d0 + 4(r%4) .. +3], lane c gets
 // V[k0 + e][d0 + c] for e = 0..3: four keys of its own column.
 
-template <typename T, int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+template <typename T, int D, int BC, int WAVES, bool CAUSAL>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource types exist only in the device pass
-    constexpr int NT = 256, QPW = 32, BR = 4 * QPW;
+    constexpr int NT = 64 * WAVES, QPW = 32, BR = WAVES * QPW;
     constexpr int KB = BC / 32;       // 32-key row blocks of S^T per tile
     constexpr int DB = D / 32;        // 32-dim row blocks of O^T
     constexpr int DS = D / 16;        // k-steps of S^T = K Q^T
@@ -432,21 +433,24 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
 
 // ------------------------------------------------------------------ dispatch ---
 
-template <typename T, int D, int BC>
+template <typename T, int D, int BC, int WAVES>
 static hipError_t launch_t(const FwdArgs& a, int causal, hipStream_t st) {
-    const dim3 grid((unsigned)a.n_blocks), block(256);
+    const dim3 grid((unsigned)a.n_blocks), block(64 * WAVES);
     if (causal)
-        hipLaunchKernelGGL((fwd_kernel<T, D, BC, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((fwd_kernel<T, D, BC, WAVES, true>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((fwd_kernel<T, D, BC, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((fwd_kernel<T, D, BC, WAVES, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
+// The compiled (d, Bc, waves) shapes; the chooser only emits these.
 template <typename T>
 static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int causal, hipStream_t st) {
-    (void)p;
-    if (d == 128) return launch_t<T, 128, 64>(a, causal, st);
-    return launch_t<T, 64, 128>(a, causal, st);
+    if (d == 128 && p.block_k == 128 && p.waves == 8) return launch_t<T, 128, 128, 8>(a, causal, st);
+    if (d == 64 && p.block_k == 128 && p.waves == 8) return launch_t<T, 64, 128, 8>(a, causal, st);
+    if (d == 128 && p.block_k == 64 && p.waves == 4) return launch_t<T, 128, 64, 4>(a, causal, st);
+    if (d == 64 && p.block_k == 128 && p.waves == 4) return launch_t<T, 64, 128, 4>(a, causal, st);
+    return hipErrorInvalidConfiguration;
 }
 
 }  // namespace fa

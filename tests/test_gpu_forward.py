@@ -153,3 +153,38 @@ def test_empty_problem_is_a_no_op(gpu_lib):
     z = torch.zeros(2, 3, 0, 64, dtype=torch.bfloat16, device="cuda")
     o, lse = gpu_lib.fa_fwd(z, z, z)
     assert o.shape == z.shape and lse.shape == (2, 3, 0)
+
+
+# ------------------------------------------- 8-wave plan: long rows, ragged tails ---
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,causal", [(2049, False), (3000, False), (8191, False), (2500, True)])
+def test_eight_wave_plan_sampled(gpu_lib, dtype, d, N, causal):
+    # B*H = 64 puts these on the 8-wave, 128-key-tile plan; rows past the last full query
+    # block and keys past the last full tile exercise the masks.
+    import torch
+
+    B, H = 4, 16
+    plan = gpu_lib.fa_fwd_plan(B, H, N, d, wl_dtype_code(dtype), causal=causal)
+    assert plan["waves"] == 8 and plan["block_k"] == 128
+    q, k, v = _random_qkv(B, H, N, d, dtype, seed=N * 7 + d + int(causal))
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    o, lse = gpu_lib.fa_fwd(tq, tk, tv, causal=causal)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng([N, d])
+    for b, h in ((0, 0), (1, 7), (3, 15)):
+        rows = np.unique(np.concatenate([[0, 255, 256, N - 257, N - 256, N - 1], rng.choice(N, 40, replace=False)]))
+        rows = rows[(rows >= 0) & (rows < N)]
+        rr = torch.from_numpy(rows).cuda()
+        Og = to_host(o[b, h].index_select(0, rr))
+        Lg = lse[b, h].index_select(0, rr).cpu().numpy().astype(np.float64)
+        O_ref, L_ref = attention_rows(q[b, h], k[b, h], v[b, h], scale_of(d), rows, causal=causal)
+        compare(Og, Lg, O_ref, L_ref, dtype, f"N={N} d={d} {dtype} causal={causal} b{b} h{h}")
+    assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
+
+
+def wl_dtype_code(dtype):
+    import online_softmax_attention_fa_amd as fa
+
+    return {"fp32": fa.FA_F32, "fp16": fa.FA_F16, "bf16": fa.FA_BF16}[dtype]
