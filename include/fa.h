@@ -106,6 +106,29 @@ fa_status fa_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype
                       int causal, fa_plan* plan);
 
 /*
+ * Split-KV forward ("从零理解Flash Attention中的online softmax", section 8.1: two-level
+ * blocking; "FlashAttention 硬件感知计算剖析", section 二: merging blocks by their
+ * maximum and sum).  The key range of every query block is cut into `splits` ranges of
+ * whole key tiles, each computed by its own workgroup into normalised fp32 partials
+ * (O_s, LSE_s) in `workspace`; a merge pass writes LSE = ln sum_s e^{LSE_s} and
+ * O = sum_s e^{LSE_s - LSE} O_s.  For problems whose plain grid does not fill the chip
+ * (small B*H*N).  Same inputs, outputs, layouts and validation as fa_fwd (non-causal),
+ * bf16/fp16 only (FA_F32 -> FA_ERR_UNSUPPORTED).  splits: 0 = the library's choice
+ * (fa_fwd_splitkv_splits), else 1..64 (more than the key tiles is clamped to them;
+ * outside -> FA_ERR_SHAPE).  With one split it is fa_fwd and needs no workspace.
+ * workspace: device memory of at least fa_fwd_splitkv_workspace_bytes(...) bytes,
+ * 256-byte aligned, owned by the caller, contents on entry ignored; NULL, short or
+ * misaligned -> FA_ERR_WORKSPACE.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype,
+                                      int32_t splits);
+/* The split count fa_fwd_splitkv uses for splits = 0 (1: splitting would not pay). */
+int32_t fa_fwd_splitkv_splits(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype);
+fa_status fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                         void* workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
+                         float scale, fa_dtype dtype, int32_t splits, void* stream);
+
+/*
  * Workspace the backward needs, in bytes: two fp32 values per row (B*H*N rows).
  * Returns 0 for invalid or empty shapes.
  */

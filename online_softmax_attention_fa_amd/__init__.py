@@ -24,8 +24,8 @@ STATUS = {
 }
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_causal", "fa_fwd_plan", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal",
-           "fa_status_str", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_causal", "fa_fwd_plan", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_splits",
+           "fa_fwd_splitkv", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal", "fa_status_str", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -64,6 +64,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).restype = I
     lib.fa_fwd_plan.argtypes = [I64, I64, I64, I64, I, I, ctypes.POINTER(Plan)]
     lib.fa_fwd_plan.restype = I
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [I64, I64, I64, I64, I, ctypes.c_int32]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_splitkv_splits.argtypes = [I64, I64, I64, I64, I]
+    lib.fa_fwd_splitkv_splits.restype = ctypes.c_int32
+    lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, P, ctypes.c_size_t, I64, I64, I64, I64, F, I, ctypes.c_int32, P]
+    lib.fa_fwd_splitkv.restype = I
     lib.fa_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     bwd_args = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, I64, I64, I64, I64, F, I, P]
@@ -153,6 +159,46 @@ def fa_fwd(q, k, v, o=None, lse=None, scale=None, stream=None, causal=False):
 
 def fa_fwd_causal(q, k, v, o=None, lse=None, scale=None, stream=None):
     return fa_fwd(q, k, v, o=o, lse=lse, scale=scale, stream=stream, causal=True)
+
+
+def fa_fwd_splitkv_workspace_bytes(B, H, N, d, dtype, splits=0) -> int:
+    """Bytes of device workspace ``fa_fwd_splitkv`` needs for ``splits`` key ranges."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(load().fa_fwd_splitkv_workspace_bytes(B, H, N, d, code, splits))
+
+
+def fa_fwd_splitkv_splits(B, H, N, d, dtype) -> int:
+    """The split count ``fa_fwd_splitkv`` picks for ``splits=0``."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(load().fa_fwd_splitkv_splits(B, H, N, d, code))
+
+
+def fa_fwd_splitkv(q, k, v, o=None, lse=None, splits=0, workspace=None, scale=None, stream=None):
+    """O, LSE = attention(q, k, v) with the key range cut into ``splits`` parts that are
+    computed separately and merged by their LSE (``fa_fwd_splitkv``).  Returns (o, lse)."""
+    import torch
+
+    lib = load()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("o must be contiguous, shaped and typed like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    code = dtype_code(q.dtype)
+    need = int(lib.fa_fwd_splitkv_workspace_bytes(B, H, N, d, code, splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                workspace.data_ptr(), workspace.numel(), B, H, N, d, float(scale), code,
+                                int(splits), _stream_handle(stream))
+    _check(st, "fa_fwd_splitkv")
+    return o, lse
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:

@@ -77,7 +77,51 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
     a.n_qblk = (int)fa::ceil_div(N, plan.block_q);
     a.n_blocks = (int)plan.grid;
     a.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+    a.splits = 1;
+    a.tiles_per_split = 0;
+    a.o_part = nullptr;
+    a.lse_part = nullptr;
     const int e = fa_launch_fwd(a, plan, dtype, (int)d, causal, stream);
+    return e == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, float* LSE, void* ws,
+                         size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                         fa_dtype dtype, int32_t splits, void* stream) {
+    fa_status st = check_problem(B, H, N, d, dtype);
+    if (st != FA_OK) return st;
+    if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+    if (splits < 0 || splits > fa::kMaxKvSplits) return FA_ERR_SHAPE;
+    if (B * H * N == 0) return FA_OK;
+    if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
+        return FA_ERR_ALIGN;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+    if (splits == 0) splits = fa::choose_kv_splits(B, H, N, d);
+    const int64_t tiles = fa::ceil_div(N, fa::splitkv_block_k(d));
+    if (splits > tiles) splits = (int32_t)tiles;
+    if (splits <= 1) return fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, dtype, stream, 0);
+    const size_t need = fa::splitkv_workspace_bytes(B, H, N, d, splits);
+    if (!ws || !aligned(ws, 256) || ws_bytes < need) return FA_ERR_WORKSPACE;
+    st = check_device();
+    if (st != FA_OK) return st;
+
+    fa::FwdArgs a;
+    a.q = Q;
+    a.k = K;
+    a.v = V;
+    a.o = O;
+    a.lse = LSE;
+    a.n = (int)N;
+    a.n_qblk = (int)fa::ceil_div(N, 128);
+    a.splits = splits;
+    a.tiles_per_split = (int)fa::ceil_div(tiles, splits);
+    a.n_blocks = (int)(B * H * a.n_qblk * splits);
+    a.c = (float)((double)scale * 1.4426950408889634074);
+    const size_t o_bytes = (size_t)splits * (size_t)(B * H * N) * (size_t)d * sizeof(float);
+    a.o_part = reinterpret_cast<float*>(ws);
+    a.lse_part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) + (o_bytes + 255) / 256 * 256);
+    const int e = fa_launch_fwd_splitkv(a, B * H * N, dtype, (int)d, stream);
     return e == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -123,6 +167,26 @@ fa_status bwd_common(const void* Q, const void* K, const void* V, const void* O,
 }  // namespace
 
 extern "C" {
+
+size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype, int32_t splits) {
+    if (check_problem(B, H, N, d, dtype) != FA_OK || dtype == FA_F32) return 0;
+    if (splits < 0 || splits > fa::kMaxKvSplits || B * H * N == 0) return 0;
+    if (splits == 0) splits = fa::choose_kv_splits(B, H, N, d);
+    const int64_t tiles = fa::ceil_div(N, fa::splitkv_block_k(d));
+    if (splits > tiles) splits = (int32_t)tiles;
+    return fa::splitkv_workspace_bytes(B, H, N, d, splits);
+}
+
+int32_t fa_fwd_splitkv_splits(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype) {
+    if (check_problem(B, H, N, d, dtype) != FA_OK || dtype == FA_F32 || B * H * N == 0) return 1;
+    return fa::choose_kv_splits(B, H, N, d);
+}
+
+fa_status fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, void* workspace,
+                         size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
+                         int32_t splits, void* stream) {
+    return splitkv_common(Q, K, V, O, LSE, workspace, ws_bytes, B, H, N, d, scale, dtype, splits, stream);
+}
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype) {
     if (check_problem(B, H, N, d, dtype) != FA_OK) return 0;

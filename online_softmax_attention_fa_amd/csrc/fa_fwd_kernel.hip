@@ -55,7 +55,7 @@ namespace fa {
 // so if lane r of the group addresses V[k0 + r/4][d0 + 4(r%4) .. +3], lane c gets
 // V[k0 + e][d0 + c] for e = 0..3: four keys of its own column.
 
-template <typename T, int D, int BC, int WAVES, bool CAUSAL>
+template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource types exist only in the device pass
     constexpr int NT = 64 * WAVES, QPW = 32, BR = WAVES * QPW;
@@ -69,6 +69,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
     constexpr int STAGE = 2 * TILE;
     constexpr int LOADS = TILE / (NT * 16);   // direct loads per thread per tile, K or V
     static_assert(LOADS >= 1 && TILE % (NT * 16) == 0, "tile must be whole 4 KiB blocks");
+    static_assert(!(SPLIT && CAUSAL), "split-KV is non-causal");
 
     // Two stages in two separate arrays: the compiler can then prove that the copies
     // into one stage do not alias the reads of the other and adds no wait for them.
@@ -84,8 +85,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
     const int N = a.n;
 
     const int bid = remap_xcd(blockIdx.x, a.n_blocks);
-    const int bh = bid / a.n_qblk;
-    int qblk = bid - bh * a.n_qblk;
+    // split-KV: the splits of one query block are neighbours in the grid (same XCD, L2)
+    const int nsplit = SPLIT ? a.splits : 1;
+    const int bh = bid / (a.n_qblk * nsplit);
+    const int rem = bid - bh * (a.n_qblk * nsplit);
+    int qblk = rem / nsplit;
+    const int split = rem - qblk * nsplit;
     if (CAUSAL) qblk = a.n_qblk - 1 - qblk;   // longest rows first
     const int64_t head = (int64_t)bh * N * D;
     const T* __restrict__ Qh = reinterpret_cast<const T*>(a.q) + head;
@@ -164,6 +169,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
 
     int n_tiles = (N + BC - 1) / BC;
     if (CAUSAL) n_tiles = min(n_tiles, (min(N, (qblk + 1) * BR) + BC - 1) / BC);
+    int t0 = 0;   // first key tile of this workgroup
+    if (SPLIT) {
+        t0 = split * a.tiles_per_split;
+        n_tiles = min(n_tiles, t0 + a.tiles_per_split);
+    }
 
     auto compute_tile = [&](int j, const lds_u8* sbase) {
         const int kbase = j * BC;
@@ -275,11 +285,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
         __builtin_amdgcn_s_setprio(0);
     };
 
-    if (n_tiles > 0) issue_tile(0, stage0);
+    if (t0 < n_tiles) issue_tile(t0, stage0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's LDS copies have landed
     __syncthreads();
 
-    for (int j = 0; j < n_tiles; j += 2) {
+    for (int j = t0; j < n_tiles; j += 2) {
         // stage 0 holds tile j; tile j + 1 streams into stage 1 meanwhile
         if (j + 1 < n_tiles) issue_tile(j + 1, stage1);
         if (!CAUSAL || j * BC <= q_wave + QPW - 1) compute_tile(j, stage0);
@@ -296,6 +306,24 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
     // ---- epilogue: O / l, LSE = (m + log2 l) ln 2
     const float lt = pair_sum(lsum);
     const float inv = 1.0f / pair_sum(lrnd);
+    if (SPLIT) {   // normalised fp32 partials of this key range (an empty range: O 0, LSE -inf)
+        if (query < N) {
+            const bool empty = t0 >= n_tiles;
+            const int64_t prow = ((int64_t)split * (a.n_blocks / (a.n_qblk * nsplit)) + bh) * N + query;
+            float* orow = a.o_part + prow * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = empty ? 0.f : o[db][4 * g + e] * inv;
+                    *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * h) = w;
+                }
+            if (h == 0) a.lse_part[prow] = empty ? -INFINITY : (m + __builtin_amdgcn_logf(lt)) * kLn2;
+        }
+        return;
+    }
     if (query < N) {
         T* orow = Oh + (int64_t)query * D;
 #pragma unroll
@@ -310,6 +338,54 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
         if (h == 0) Lh[query] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
     }
 #endif
+}
+
+// ---------------------------------------------------------- split-KV merge ---
+//
+// Combines the normalised partials of the key ranges by their log-sum-exp, the two-block
+// merge of "FlashAttention 硬件感知计算剖析" (section 二) generalised to S parts:
+//     LSE = ln sum_s e^{LSE_s},   O = sum_s e^{LSE_s - LSE} O_s.
+// D / 8 lanes per row, 8 dims (two 16-byte loads per partial) each.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ o_part,
+                                                            const float* __restrict__ lse_part, T* __restrict__ O,
+                                                            float* __restrict__ LSE, int64_t rows, int splits) {
+    constexpr int LPR = D / 8, RPB = 256 / LPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int part = threadIdx.x % LPR;
+    if (row >= rows) return;
+    float mx = -INFINITY;
+    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, lse_part[(int64_t)s * rows + row]);
+    float den = 0.f;
+    for (int s = 0; s < splits; ++s) den += __expf(lse_part[(int64_t)s * rows + row] - mx);
+    const float lse = mx + __logf(den);
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < splits; ++s) {
+        const float w = __expf(lse_part[(int64_t)s * rows + row] - lse);
+        const float* src = o_part + ((int64_t)s * rows + row) * D + part * 8;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        a0 += w * x0;
+        a1 += w * x1;
+    }
+    u32x4 out;
+    out[0] = Elt<T>::pack2(a0[0], a0[1]);
+    out[1] = Elt<T>::pack2(a0[2], a0[3]);
+    out[2] = Elt<T>::pack2(a1[0], a1[1]);
+    out[3] = Elt<T>::pack2(a1[2], a1[3]);
+    *reinterpret_cast<u32x4*>(O + row * D + part * 8) = out;
+    if (part == 0) LSE[row] = lse;
+}
+
+template <typename T, int D, int BC>
+static hipError_t launch_splitkv_t(const FwdArgs& a, int64_t rows, hipStream_t st) {
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, 4, false, true>), dim3((unsigned)a.n_blocks), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((splitkv_merge_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                       a.o_part, a.lse_part, reinterpret_cast<T*>(a.o), a.lse, rows, a.splits);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------- fp32 kernel ---
@@ -454,6 +530,17 @@ static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int cau
 }
 
 }  // namespace fa
+
+int fa_launch_fwd_splitkv(const fa::FwdArgs& a, int64_t rows, int dtype, int d, void* stream) {
+    using namespace fa;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == FA_BF16)
+        e = d == 128 ? launch_splitkv_t<__bf16, 128, 64>(a, rows, st) : launch_splitkv_t<__bf16, 64, 128>(a, rows, st);
+    else
+        e = d == 128 ? launch_splitkv_t<_Float16, 128, 64>(a, rows, st) : launch_splitkv_t<_Float16, 64, 128>(a, rows, st);
+    return (int)e;
+}
 
 int fa_launch_fwd(const fa::FwdArgs& a, const fa_plan& plan, int dtype, int d, int causal, void* stream) {
     using namespace fa;

@@ -21,8 +21,14 @@ struct FwdArgs {
     float* lse;
     int n;          // sequence length N
     int n_qblk;     // ceil(N / Br)
-    int n_blocks;   // workgroups in the grid = B*H*n_qblk
+    int n_blocks;   // workgroups in the grid = B*H*n_qblk (*splits)
     float c;        // scale * log2(e): scores are taken to base 2 inside the kernel
+    // split-KV only: key tiles [s*tiles_per_split, (s+1)*tiles_per_split) per split s;
+    // normalised fp32 partial O [splits][B*H*N][d] and partial LSE [splits][B*H*N]
+    int splits;
+    int tiles_per_split;
+    float* o_part;
+    float* lse_part;
 };
 
 // Kernel arguments of the backward pass.
@@ -108,11 +114,38 @@ inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int d
     return p;
 }
 
+// Split-KV (key ranges processed by separate workgroups, then merged by their LSE).
+constexpr int kMaxKvSplits = 64;
+// Key tile of the split-KV path (the 4-wave tile-loop kernel's Bc).
+inline int splitkv_block_k(int64_t d) { return d == 128 ? 64 : 128; }
+// Workspace of fa_fwd_splitkv: partial O (fp32) and partial LSE per split, 256-byte aligned.
+inline size_t splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int splits) {
+    if (splits <= 1) return 0;
+    const size_t rows = (size_t)(B * H * N);
+    const size_t o_bytes = (size_t)splits * rows * (size_t)d * sizeof(float);
+    const size_t l_bytes = (size_t)splits * rows * sizeof(float);
+    return (o_bytes + 255) / 256 * 256 + (l_bytes + 255) / 256 * 256;
+}
+// The chooser's split count: enough workgroups for two per CU, each split at least two
+// key tiles; 1 when the plain grid already fills the chip.
+inline int choose_kv_splits(int64_t B, int64_t H, int64_t N, int64_t d) {
+    const int64_t grid = B * H * ceil_div(N, 128);
+    const int64_t tiles = ceil_div(N, splitkv_block_k(d));
+    if (grid >= 2 * kCus) return 1;
+    int64_t s = ceil_div(2 * kCus, grid);
+    if (s > tiles / 2) s = tiles / 2;
+    if (s > kMaxKvSplits) s = kMaxKvSplits;
+    return s < 2 ? 1 : (int)s;
+}
+
 }  // namespace fa
 
 // Launchers implemented in fa_fwd_kernel.hip.  Return 0 on success or the
 // hipError_t of the launch.
 int fa_launch_fwd(const fa::FwdArgs& a, const fa_plan& plan, int dtype, int d, int causal,
                   void* stream);
+// Split-KV forward (bf16/fp16, non-causal): a.splits > 1, a.o_part / a.lse_part set;
+// launches the partial kernel and the merge.  rows = B*H*N.
+int fa_launch_fwd_splitkv(const fa::FwdArgs& a, int64_t rows, int dtype, int d, void* stream);
 // rows = B*H*N.  Launches the preprocess, dQ and dK/dV kernels in stream order.
 int fa_launch_bwd(const fa::BwdArgs& a, int64_t rows, int dtype, int d, int causal, void* stream);

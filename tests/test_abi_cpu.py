@@ -188,3 +188,50 @@ def test_library_has_no_torch_dependency():
     out = subprocess.run(["ldd", fa.LIB_PATH], capture_output=True, text=True).stdout
     names = [line.split()[0] for line in out.splitlines() if line.strip()]   # not the load addresses
     assert names and not any("torch" in n or n.startswith("libc10") for n in names), names
+
+
+def _skv(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=WS, ws_bytes=1 << 40, B=1, H=1, N=4096, d=128,
+         scale=0.125, dtype=fa.FA_BF16, splits=4):
+    return lib.fa_fwd_splitkv(q, k, v, o, lse, ws, ws_bytes, B, H, N, d, scale, dtype, splits, None)
+
+
+def test_splitkv_workspace_and_split_choice(lib):
+    # partial O (fp32, d per row) and partial LSE per split, each rounded up to 256 bytes
+    rows = 2 * 3 * 1000
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 3, 1000, 64, fa.FA_BF16, 4) == \
+        -(-4 * rows * 64 * 4 // 256) * 256 + -(-4 * rows * 4 // 256) * 256
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 3, 1000, 64, fa.FA_BF16, 1) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 3, 1000, 64, fa.FA_F32, 4) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 3, 1000, 64, fa.FA_BF16, 65) == 0
+    # more splits than key tiles are clamped to the tiles (300 keys / 64 = 5 tiles at d=128)
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, 300, 128, fa.FA_BF16, 64) == \
+        lib.fa_fwd_splitkv_workspace_bytes(1, 1, 300, 128, fa.FA_BF16, 5)
+    # the chooser: a small grid is split, a full one is not; every split keeps >= 2 tiles
+    assert lib.fa_fwd_splitkv_splits(1, 1, 16384, 128, fa.FA_BF16) > 1
+    assert lib.fa_fwd_splitkv_splits(4, 32, 16384, 128, fa.FA_BF16) == 1
+    for N in (128, 256, 1000, 4097, 16384):
+        s = lib.fa_fwd_splitkv_splits(1, 1, N, 128, fa.FA_BF16)
+        assert 1 <= s <= 64 and (s == 1 or -(-N // 64) >= 2 * s)
+
+
+def test_splitkv_validation(lib):
+    assert _skv(lib, dtype=fa.FA_F32) == 3
+    assert _skv(lib, d=80) == 3
+    assert _skv(lib, splits=-1) == 2
+    assert _skv(lib, splits=65) == 2
+    assert _skv(lib, N=0, q=None, ws=None) == 0
+    assert _skv(lib, q=None) == 1
+    assert _skv(lib, o=FAKE + 8) == 4
+    assert _skv(lib, scale=0.0) == 5
+    assert _skv(lib, ws=None) == 8
+    assert _skv(lib, ws=WS + 64) == 8
+    assert _skv(lib, ws_bytes=16) == 8
+
+
+def test_splitkv_valid_call_without_gpu_stops_at_device_check(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; the device check passes")
+    assert _skv(lib) == 6
+    assert _skv(lib, splits=1, ws=None) == 6   # one split is fa_fwd: no workspace needed
