@@ -1,7 +1,7 @@
 """Benchmark of the fused attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-backward] [--copy-calibration BYTES]
+                    [--no-backward] [--copy-calibration BYTES] [--sweep]
 
 Workload: B=4, H=32, N=16384, d=128, bf16 Q/K/V, scale 1/sqrt(d), non-causal, one
 forward per step through the C ABI (fa_fwd) with inputs resident in HBM.  Prints
@@ -19,6 +19,10 @@ ONE JSON line on stdout (everything else goes to stderr):
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload (whole heads
              in row chunks, all keys, about 15 s of host time), timed on the host
              cores, with the GPU output checked on the same rows
+  sweep      (--sweep only) forward time of the smaller workloads (fp32 B1 H1 N256 d64,
+             bf16 B4 H16 N2048 d64, fp16 B1 H32 N16384 d128, bf16 B2 H8 N4097 d128), the
+             causal and split-KV variants, and short sequences at B*H=1024 d=128 where
+             the kernel is bounded by HBM bandwidth; min and median of per-launch events
 """
 
 from __future__ import annotations
@@ -109,6 +113,7 @@ def cpu_baseline(q, k, v, o, lse, scale, budget_s=15.0, chunk=2048):
         if spent >= budget_s:
             break
     flops = 4.0 * rows_done * N * D
+    full_s = 4.0 * B * H * N * N * D / (flops / spent)
     return {
         "value": flops / spent / 1e12,
         "unit": "TFLOP/s",
@@ -118,6 +123,7 @@ def cpu_baseline(q, k, v, o, lse, scale, budget_s=15.0, chunk=2048):
                   f"workload against all {N} keys: 4*rows*N*d = {flops:.3e} FLOP of fp64 numpy "
                   f"three-pass attention in {spent:.1f} s",
         "seconds": round(spent, 2),
+        "extrapolated_full_workload_s": round(full_s, 1),
         "gpu_rows_max_err_o": err_o,
         "gpu_rows_max_err_lse": err_l,
     }
@@ -150,6 +156,72 @@ def time_backward(fa, q, k, v, o, lse, scale, stream, steps):
             "outputs_finite": ok}
 
 
+def launch_times(fn, stream, steps, warmup=5):
+    """Per-launch durations (ms) from events recorded between back-to-back launches."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def sweep(fa, stream, steps=20):
+    """Forward timings of the smaller workloads and the bandwidth-bound short sequences."""
+    import statistics
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(7)
+    cases = [
+        ("fp32 B1 H1 N256 d64", 1, 1, 256, 64, torch.float32, "plain"),
+        ("bf16 B4 H16 N2048 d64", 4, 16, 2048, 64, torch.bfloat16, "plain"),
+        ("fp16 B1 H32 N16384 d128", 1, 32, 16384, 128, torch.float16, "plain"),
+        ("bf16 B2 H8 N4097 d128", 2, 8, 4097, 128, torch.bfloat16, "plain"),
+        ("bf16 B4 H32 N16384 d128 causal", 4, 32, 16384, 128, torch.bfloat16, "causal"),
+        ("bf16 B1 H1 N16384 d128", 1, 1, 16384, 128, torch.bfloat16, "plain"),
+        ("bf16 B1 H1 N16384 d128 split-KV", 1, 1, 16384, 128, torch.bfloat16, "split"),
+        ("bf16 B1 H8 N4096 d128", 1, 8, 4096, 128, torch.bfloat16, "plain"),
+        ("bf16 B1 H8 N4096 d128 split-KV", 1, 8, 4096, 128, torch.bfloat16, "split"),
+    ] + [(f"bf16 B16 H64 N{n} d128", 16, 64, n, 128, torch.bfloat16, "plain") for n in (128, 256, 512)]
+    rows = []
+    for name, b, h, n, d, dt, mode in cases:
+        q, k, v = (torch.randn(b, h, n, d, device=dev, dtype=dt, generator=gen) for _ in range(3))
+        o = torch.empty_like(q)
+        lse = torch.empty(b, h, n, device=dev, dtype=torch.float32)
+        sc = 1.0 / math.sqrt(d)
+        if mode == "split":
+            splits = fa.fa_fwd_splitkv_splits(b, h, n, d, dt)
+            ws = torch.empty(max(1, fa.fa_fwd_splitkv_workspace_bytes(b, h, n, d, dt, splits)),
+                             dtype=torch.uint8, device=dev)
+            fn = lambda: fa.fa_fwd_splitkv(q, k, v, o, lse, splits=splits, workspace=ws, scale=sc, stream=stream)
+        else:
+            fn = lambda: fa.fa_fwd(q, k, v, o, lse, scale=sc, stream=stream, causal=(mode == "causal"))
+        t = launch_times(fn, stream, steps)
+        tmin, tmed = min(t), statistics.median(t)
+        flops = 4.0 * b * h * n * n * d * (0.5 if mode == "causal" else 1.0)
+        nbytes = 4.0 * b * h * n * d * q.element_size() + 4.0 * b * h * n
+        peak = 157.3 if dt == torch.float32 else PEAK_BF16_TFLOPS
+        r = {"case": name, "min_ms": round(tmin, 4), "median_ms": round(tmed, 4),
+             "tflops": round(flops / (tmed * 1e-3) / 1e12, 2),
+             "pct_of_mfma_peak": round(100 * flops / (tmed * 1e-3) / 1e12 / peak, 2),
+             "gbps": round(nbytes / (tmed * 1e-3) / 1e9, 1)}
+        if mode == "split":
+            r["splits"] = splits
+        rows.append(r)
+        log(f"sweep {name}: median {tmed * 1e3:.1f} us, min {tmin * 1e3:.1f} us, {r['tflops']} TFLOP/s "
+            f"({r['pct_of_mfma_peak']}% of MFMA peak), {r['gbps']} GB/s algorithmic")
+        del q, k, v, o, lse
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -158,6 +230,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
+    ap.add_argument("--sweep", action="store_true", help="also time the smaller workloads")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -200,17 +273,19 @@ def main():
         fa.fa_fwd(q, k, v, o, lse, scale=scale, stream=stream)
     torch.cuda.synchronize()
 
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive launches: the sum is the bracketed time, the
+    # differences give per-launch min and median
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         fa.fa_fwd(q, k, v, o, lse, scale=scale, stream=stream)
-    end.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = start.elapsed_time(end) / args.steps
+    kernel_ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_launch = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     ms_per_step = max(kernel_ms, wall * 1e3 / args.steps)
 
     flops = 4.0 * B * H * N * N * D
@@ -237,6 +312,8 @@ def main():
                                "scale=1/sqrt(d), LSE saved", "B": B, "H": H, "N": N, "d": D,
                    "causal": False, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
+        "launch_ms": {"mean": round(kernel_ms, 4), "min": round(per_launch[0], 4),
+                      "median": round(per_launch[len(per_launch) // 2], 4)},
         "plan": plan,
         "roofline": {
             "bound": "mfma",
@@ -249,6 +326,8 @@ def main():
     }
     if not args.no_backward:
         out["backward"] = time_backward(fa, q, k, v, o, lse, scale, stream, args.backward_steps)
+    if args.sweep:
+        out["sweep"] = sweep(fa, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, o, lse, scale)
     print(json.dumps(out), flush=True)
