@@ -8,6 +8,8 @@ Every function follows the plain definition of attention written out in float64
 (see ``oracle.attention`` for the page citations of each step).  Every function here
 is pinned by the CPU tests in ``tests/test_oracle_*.py`` against closed forms,
 invariants, an independent library routine or brute force; none is "parity unpinned".
+``oracle.fp8`` (the E4M3 format, block quantisation and attention on dequantised
+tensors) is imported by name; it is pinned by ``tests/test_oracle_fp8.py``.
 """
 
 from .attention import (  # noqa: F401
