@@ -16,6 +16,10 @@ ONE JSON line on stdout (everything else goes to stderr):
   backward   the recompute-based backward (fa_bwd) on the same tensors with seeded dO,
              timed separately after the forward; TFLOP/s counted as 10*B*H*N^2*d
              (2.5x the forward: S, dP, dV, dK, dQ), not part of `value`
+  fp8        the opt-in block-scaled fp8 forward (fa_fwd_fp8) on the same inputs quantised
+             once by fa_quantize_fp8 (codes resident in HBM, like a cached K/V); TFLOP/s
+             counted as 4*B*H*N^2*d against the dense fp8 MFMA peak; the quantiser's time is
+             reported beside it, not inside it
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload (whole heads
              in row chunks, all keys, about 15 s of host time), timed on the host
              cores, with the GPU output checked on the same rows
@@ -41,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) and % of MI355X bf16 MFMA peak, d=128"
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2           # MI355X dense fp8 MFMA: 256 CU x 8192 FLOP/clk x 2.4 GHz
 B, H, N, D = 4, 32, 16384, 128
 KERNEL_SOURCES = ("online_softmax_attention_fa_amd/csrc/fa_fwd_kernel.hip",
                   "online_softmax_attention_fa_amd/csrc/fa_device.h",
@@ -156,6 +161,35 @@ def time_backward(fa, q, k, v, o, lse, scale, stream, steps):
             "outputs_finite": ok}
 
 
+def time_fp8(fa, q, k, v, o_ref, scale, stream, steps):
+    """fa_quantize_fp8 of Q, K, V once, then fa_fwd_fp8 timed with events on the stream."""
+    import torch
+
+    def quantize():
+        return (fa.fa_quantize_fp8(q, stream=stream), fa.fa_quantize_fp8(k, stream=stream),
+                fa.fa_quantize_fp8(v, transpose=True, stream=stream))
+
+    (q8, qs), (k8, ks), (vt8, vs) = quantize()
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
+    fwd = lambda: fa.fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, o, lse, scale=scale, stream=stream)
+    fwd()
+    torch.cuda.synchronize()
+    t_q = launch_times(quantize, stream, 3, warmup=1)
+    t = launch_times(fwd, stream, steps, warmup=2)
+    ms = sum(t) / len(t)
+    flops = 4.0 * B * H * N * N * D
+    tflops = flops / (ms * 1e-3) / 1e12
+    diff = (o.float() - o_ref.float()).abs().max().item()
+    ok = bool(torch.isfinite(o).all().item() and torch.isfinite(lse).all().item())
+    log(f"fp8 forward {ms:.3f} ms/launch, {tflops:.1f} TFLOP/s = {100 * tflops / PEAK_FP8_TFLOPS:.1f}% of the fp8 "
+        f"peak; quantise Q, K, V {sum(t_q) / len(t_q):.3f} ms; max |O_fp8 - O_bf16| = {diff:.3e}")
+    return {"ms_per_launch": round(ms, 4), "min_ms": round(min(t), 4), "tflops": round(tflops, 2),
+            "peak": PEAK_FP8_TFLOPS, "frac_of_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+            "quantize_qkv_ms": round(sum(t_q) / len(t_q), 4), "max_abs_diff_vs_bf16_o": diff,
+            "outputs_finite": ok, "steps": steps}
+
+
 def launch_times(fn, stream, steps, warmup=5):
     """Per-launch durations (ms) from events recorded between back-to-back launches."""
     import torch
@@ -231,6 +265,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--sweep", action="store_true", help="also time the smaller workloads")
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--fp8-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -326,6 +362,8 @@ def main():
     }
     if not args.no_backward:
         out["backward"] = time_backward(fa, q, k, v, o, lse, scale, stream, args.backward_steps)
+    if not args.no_fp8:
+        out["fp8"] = time_fp8(fa, q, k, v, o, scale, stream, args.fp8_steps)
     if args.sweep:
         out["sweep"] = sweep(fa, stream)
     if not args.no_cpu_baseline:

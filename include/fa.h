@@ -158,6 +158,48 @@ fa_status fa_bwd_causal(const void* Q, const void* K, const void* V, const void*
                         int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
                         void* stream);
 
+/*
+ * Block-scaled fp8 mode (opt-in; changes the numerics).  "从零理解Flash Attention中的online
+ * softmax" (section 9.1) keeps K and V in 8 bits with a scale and dequantises each tile on
+ * load; "FlashAttention 硬件感知计算剖析" (its FlashAttention-3 summary) names native FP8
+ * with block-wise scale factors.  The reading taken here:
+ *   - codes are OCP E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
+ *     finite 448; S.1111.111 is NaN), one byte per element;
+ *   - every 64 consecutive rows of a (batch, head) share one scale 2^e, the smallest power
+ *     of two with max|x| <= 448 * 2^e (e in [-126, 127]; an all-zero block takes -126);
+ *     a code c stands for value(c) * 2^e;
+ *   - the forward is attention of the dequantised Q, K, V; it also rounds the
+ *     probabilities to E4M3 for the P V product (fp32 accumulation throughout), so O
+ *     carries that rounding on top of the quantisation of the inputs.
+ * Scales are fp32 [B, H, nb] with nb = fa_fp8_scale_blocks(N); block k covers rows
+ * 64k .. 64k+63.  V is passed transposed, V^T [B, H, d, Np] with Np = fa_fp8_padded_len(N),
+ * keys contiguous; the padding keys N..Np-1 must hold code 0 (fa_quantize_fp8 writes it).
+ */
+/* Np: N rounded up to the forward's key tile (128); 0 for N < 0. */
+int64_t fa_fp8_padded_len(int64_t N);
+/* nb = ceil(N / 64): scale blocks per (batch, head); 0 for N < 0. */
+int64_t fa_fp8_scale_blocks(int64_t N);
+/*
+ * Quantise X [B,H,N,d] (FA_BF16 / FA_F16) into codes and block scales.  transpose = 0:
+ * X8 is [B,H,N,d]; transpose = 1: X8 is V^T [B,H,d,Np] including its zero padding.
+ * scales: fp32 [B,H,nb].  Deterministic; rounding to nearest, ties to even.  Non-finite
+ * elements give a scale of 1 for their block and NaN codes.  Errors: as fa_fwd for
+ * shapes, dtype (FA_F32 -> FA_ERR_UNSUPPORTED) and pointers (X, X8 16-byte, scales
+ * 4-byte aligned); transpose not 0/1 -> FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_quantize_fp8(const void* X, void* X8, float* scales, int64_t B, int64_t H, int64_t N,
+                          int64_t d, fa_dtype dtype, int32_t transpose, void* stream);
+/*
+ * Attention forward on block-scaled E4M3 inputs: Q8, K8 [B,H,N,d] codes, Vt8 [B,H,d,Np]
+ * codes, their scales [B,H,nb]; writes O [B,H,N,d] of out_dtype (FA_BF16 / FA_F16) and
+ * LSE [B,H,N] fp32 (natural log of the dequantised scores' exp-sum, scale included).
+ * Non-causal.  Errors: as fa_fwd (code pointers and O 16-byte aligned, scales and LSE
+ * 4-byte aligned; out_dtype FA_F32 -> FA_ERR_UNSUPPORTED).
+ */
+fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale,
+                     const float* k_scale, const float* v_scale, void* O, float* LSE, int64_t B,
+                     int64_t H, int64_t N, int64_t d, float scale, fa_dtype out_dtype, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(fa_status s);
 

@@ -25,7 +25,8 @@ STATUS = {
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_causal", "fa_fwd_plan", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_splits",
-           "fa_fwd_splitkv", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal", "fa_status_str", "fa_version")
+           "fa_fwd_splitkv", "fa_fp8_padded_len", "fa_fp8_scale_blocks", "fa_quantize_fp8", "fa_fwd_fp8",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal", "fa_status_str", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -70,6 +71,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_splitkv_splits.restype = ctypes.c_int32
     lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, P, ctypes.c_size_t, I64, I64, I64, I64, F, I, ctypes.c_int32, P]
     lib.fa_fwd_splitkv.restype = I
+    lib.fa_fp8_padded_len.argtypes = [I64]
+    lib.fa_fp8_padded_len.restype = I64
+    lib.fa_fp8_scale_blocks.argtypes = [I64]
+    lib.fa_fp8_scale_blocks.restype = I64
+    lib.fa_quantize_fp8.argtypes = [P, P, P, I64, I64, I64, I64, I, ctypes.c_int32, P]
+    lib.fa_quantize_fp8.restype = I
+    lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, P]
+    lib.fa_fwd_fp8.restype = I
     lib.fa_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     bwd_args = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, I64, I64, I64, I64, F, I, P]
@@ -198,6 +207,72 @@ def fa_fwd_splitkv(q, k, v, o=None, lse=None, splits=0, workspace=None, scale=No
                                 workspace.data_ptr(), workspace.numel(), B, H, N, d, float(scale), code,
                                 int(splits), _stream_handle(stream))
     _check(st, "fa_fwd_splitkv")
+    return o, lse
+
+
+def fa_fp8_padded_len(N) -> int:
+    """Key length of the transposed V codes: N rounded up to the fp8 forward's key tile."""
+    return int(load().fa_fp8_padded_len(N))
+
+
+def fa_fp8_scale_blocks(N) -> int:
+    """Scale blocks (of 64 rows) per (batch, head)."""
+    return int(load().fa_fp8_scale_blocks(N))
+
+
+def fa_quantize_fp8(x, transpose=False, x8=None, scales=None, stream=None):
+    """Block-scaled E4M3 codes of x [B, H, N, d] (bf16 / fp16) through ``fa_quantize_fp8``.
+
+    Returns (codes, scales): codes uint8 [B, H, N, d], or [B, H, d, Np] when ``transpose``;
+    scales fp32 [B, H, ceil(N / 64)]."""
+    import torch
+
+    lib = load()
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor [B, H, N, d]")
+    B, H, N, d = x.shape
+    shape = (B, H, d, fa_fp8_padded_len(N)) if transpose else (B, H, N, d)
+    x8 = torch.empty(shape, dtype=torch.uint8, device=x.device) if x8 is None else x8
+    scales = torch.empty((B, H, fa_fp8_scale_blocks(N)), dtype=torch.float32, device=x.device) if scales is None else scales
+    if tuple(x8.shape) != shape or x8.dtype != torch.uint8 or not x8.is_contiguous():
+        raise ValueError(f"x8 must be contiguous uint8 {shape}")
+    if tuple(scales.shape) != (B, H, fa_fp8_scale_blocks(N)) or scales.dtype != torch.float32:
+        raise ValueError("scales must be fp32 [B, H, ceil(N / 64)]")
+    with torch.cuda.device(x.device):
+        st = lib.fa_quantize_fp8(x.data_ptr(), x8.data_ptr(), scales.data_ptr(), B, H, N, d,
+                                 dtype_code(x.dtype), 1 if transpose else 0, _stream_handle(stream))
+    _check(st, "fa_quantize_fp8")
+    return x8, scales
+
+
+def fa_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, o=None, lse=None, scale=None, out_dtype=None, stream=None):
+    """O, LSE of attention on block-scaled E4M3 inputs through ``fa_fwd_fp8``.
+
+    q8, k8: uint8 [B, H, N, d]; vt8: uint8 [B, H, d, Np]; scales fp32 [B, H, nb].
+    O has ``out_dtype`` (default bfloat16).  Returns (o, lse)."""
+    import torch
+
+    lib = load()
+    B, H, N, d = q8.shape
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    nb = fa_fp8_scale_blocks(N)
+    if k8.shape != q8.shape or tuple(vt8.shape) != (B, H, d, fa_fp8_padded_len(N)):
+        raise ValueError("k8 must match q8; vt8 must be [B, H, d, Np]")
+    for t in (q8, k8, vt8):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("codes must be contiguous uint8 device tensors")
+    for t in (q_scale, k_scale, v_scale):
+        if tuple(t.shape) != (B, H, nb) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("scales must be contiguous fp32 [B, H, ceil(N / 64)]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=q8.device) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    with torch.cuda.device(q8.device):
+        st = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
+                            v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
+                            dtype_code(out_dtype), _stream_handle(stream))
+    _check(st, "fa_fwd_fp8")
     return o, lse
 
 

@@ -8,11 +8,12 @@
 #include <mutex>
 #include <string.h>
 
+#include "fa_fp8.h"
 #include "fa_internal.h"
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 constexpr int kMaxDevices = 64;
 
 struct DeviceInfo {
@@ -125,6 +126,15 @@ fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, f
     return e == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Shape checks of the fp8 mode: check_problem plus the padded V^T head in 32-bit offsets.
+fa_status check_fp8_problem(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    fa_status st = check_problem(B, H, N, d, dtype);
+    if (st != FA_OK) return st;
+    if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+    if (N > 0 && fa::fp8_padded_len(N) * d >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
 fa_status bwd_common(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                      const float* LSE, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
@@ -186,6 +196,65 @@ fa_status fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, f
                          size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
                          int32_t splits, void* stream) {
     return splitkv_common(Q, K, V, O, LSE, workspace, ws_bytes, B, H, N, d, scale, dtype, splits, stream);
+}
+
+int64_t fa_fp8_padded_len(int64_t N) { return N < 0 ? 0 : fa::fp8_padded_len(N); }
+
+int64_t fa_fp8_scale_blocks(int64_t N) { return N < 0 ? 0 : fa::fp8_scale_blocks(N); }
+
+fa_status fa_quantize_fp8(const void* X, void* X8, float* scales, int64_t B, int64_t H, int64_t N, int64_t d,
+                          fa_dtype dtype, int32_t transpose, void* stream) {
+    fa_status st = check_fp8_problem(B, H, N, d, dtype);
+    if (st != FA_OK) return st;
+    if (transpose != 0 && transpose != 1) return FA_ERR_UNSUPPORTED;
+    if (B * H * N == 0) return FA_OK;
+    if (!X || !X8 || !scales) return FA_ERR_NULL;
+    if (!aligned(X, 16) || !aligned(X8, 16) || !aligned(scales, 4)) return FA_ERR_ALIGN;
+    st = check_device();
+    if (st != FA_OK) return st;
+    fa::QuantArgs a;
+    a.x = X;
+    a.x8 = reinterpret_cast<unsigned char*>(X8);
+    a.scales = scales;
+    a.n = (int)N;
+    a.np = (int)fa::fp8_padded_len(N);
+    a.nb = (int)fa::fp8_scale_blocks(N);
+    a.blocks_per_head = transpose ? a.np / fa::kFp8Block : a.nb;
+    const int e = fa_launch_quantize_fp8(a, B * H, dtype, (int)d, transpose, stream);
+    return e == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale, const float* k_scale,
+                     const float* v_scale, void* O, float* LSE, int64_t B, int64_t H, int64_t N, int64_t d,
+                     float scale, fa_dtype out_dtype, void* stream) {
+    fa_status st = check_fp8_problem(B, H, N, d, out_dtype);
+    if (st != FA_OK) return st;
+    if (B * H * N == 0) return FA_OK;
+    if (!Q8 || !K8 || !Vt8 || !q_scale || !k_scale || !v_scale || !O || !LSE) return FA_ERR_NULL;
+    if (!aligned(Q8, 16) || !aligned(K8, 16) || !aligned(Vt8, 16) || !aligned(O, 16) || !aligned(q_scale, 4) ||
+        !aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(LSE, 4))
+        return FA_ERR_ALIGN;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+    st = check_device();
+    if (st != FA_OK) return st;
+    const bool eight = fa::fp8_eight_waves(B, H, N);
+    fa::Fp8Args a;
+    a.q8 = reinterpret_cast<const unsigned char*>(Q8);
+    a.k8 = reinterpret_cast<const unsigned char*>(K8);
+    a.vt8 = reinterpret_cast<const unsigned char*>(Vt8);
+    a.qs = q_scale;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.o = O;
+    a.lse = LSE;
+    a.n = (int)N;
+    a.np = (int)fa::fp8_padded_len(N);
+    a.nb = (int)fa::fp8_scale_blocks(N);
+    a.n_qblk = (int)fa::ceil_div(N, eight ? 256 : 128);
+    a.n_blocks = (int)(B * H * a.n_qblk);
+    a.c = (float)((double)scale * 1.4426950408889634074);
+    const int e = fa_launch_fwd_fp8(a, B * H, out_dtype, (int)d, eight ? 1 : 0, stream);
+    return e == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype) {

@@ -1,0 +1,56 @@
+// Internal declarations of the block-scaled fp8 mode, shared by the C ABI (fa_api.hip)
+// and its kernels (fa_fp8_kernel.hip).
+#pragma once
+
+#include "fa_internal.h"
+
+namespace fa {
+
+// ------------------------------------------------------------ block-scaled fp8 ---
+// Q, K and V in OCP E4M3 with one power-of-two scale per 64 rows of a (batch, head).
+constexpr int kFp8Block = 64;      // rows per scale block
+constexpr int kFp8Bc = 128;        // keys per LDS tile of the fp8 forward
+// V^T rows are padded to a whole number of key tiles (padding holds code 0).
+inline int64_t fp8_padded_len(int64_t N) { return ceil_div(N, kFp8Bc) * kFp8Bc; }
+inline int64_t fp8_scale_blocks(int64_t N) { return ceil_div(N, kFp8Block); }
+
+// Quantiser arguments.  One workgroup per (batch*head, 64-row block).
+struct QuantArgs {
+    const void* x;      // [B, H, N, d] bf16 / fp16
+    unsigned char* x8;  // [B, H, N, d] codes, or [B, H, d, Np] when transposed
+    float* scales;      // [B, H, nb]
+    int n;
+    int np;             // padded length (transposed layout only)
+    int nb;             // scale blocks per head = ceil(N / 64)
+    int blocks_per_head;   // grid blocks per head: nb, or Np / 64 when transposed
+};
+
+// fp8 forward arguments.
+struct Fp8Args {
+    const unsigned char* q8;   // [B, H, N, d]
+    const unsigned char* k8;   // [B, H, N, d]
+    const unsigned char* vt8;  // [B, H, d, Np]
+    const float* qs;           // [B, H, nb] block scales (powers of two)
+    const float* ks;
+    const float* vs;
+    void* o;                   // [B, H, N, d] bf16 / fp16
+    float* lse;                // [B, H, N]
+    int n;
+    int np;
+    int nb;
+    int n_qblk;
+    int n_blocks;
+    float c;                   // scale * log2(e)
+};
+inline bool fp8_eight_waves(int64_t B, int64_t H, int64_t N) {
+    const int64_t g8 = B * H * ceil_div(N, 8 * 32);
+    return N >= 2048 && (g8 >= 2 * kCus || g8 % kCus == 0);
+}
+
+}  // namespace fa
+
+// Launchers implemented in fa_fp8_kernel.hip (0 or the hipError_t of the launch).
+// in_dtype: input type of the quantiser; out_dtype: O's type in the forward.
+int fa_launch_quantize_fp8(const fa::QuantArgs& a, int64_t bh, int in_dtype, int d, int transpose, void* stream);
+int fa_launch_fwd_fp8(const fa::Fp8Args& a, int64_t bh, int out_dtype, int d, int eight_waves, void* stream);
+

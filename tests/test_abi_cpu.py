@@ -235,3 +235,52 @@ def test_splitkv_valid_call_without_gpu_stops_at_device_check(lib):
         pytest.skip("a GPU is visible; the device check passes")
     assert _skv(lib) == 6
     assert _skv(lib, splits=1, ws=None) == 6   # one split is fa_fwd: no workspace needed
+
+
+def _q8(lib, x=FAKE, x8=FAKE, sc=FAKE, B=1, H=2, N=100, d=128, dtype=fa.FA_BF16, transpose=0):
+    return lib.fa_quantize_fp8(x, x8, sc, B, H, N, d, dtype, transpose, None)
+
+
+def _f8(lib, q=FAKE, k=FAKE, v=FAKE, qs=FAKE, ks=FAKE, vs=FAKE, o=FAKE, lse=FAKE, B=1, H=2, N=100, d=128,
+        scale=0.125, dtype=fa.FA_BF16):
+    return lib.fa_fwd_fp8(q, k, v, qs, ks, vs, o, lse, B, H, N, d, scale, dtype, None)
+
+
+def test_fp8_sizes(lib):
+    assert lib.fa_fp8_padded_len(1) == 128 and lib.fa_fp8_padded_len(128) == 128
+    assert lib.fa_fp8_padded_len(129) == 256 and lib.fa_fp8_padded_len(0) == 0
+    assert lib.fa_fp8_padded_len(-3) == 0
+    assert lib.fa_fp8_scale_blocks(1) == 1 and lib.fa_fp8_scale_blocks(64) == 1
+    assert lib.fa_fp8_scale_blocks(65) == 2 and lib.fa_fp8_scale_blocks(16384) == 256
+    assert lib.fa_fp8_scale_blocks(0) == 0
+
+
+def test_fp8_validation_order_and_codes(lib):
+    assert _q8(lib, N=-1) == 2
+    assert _q8(lib, d=96) == 3
+    assert _q8(lib, dtype=fa.FA_F32) == 3
+    assert _q8(lib, transpose=2) == 3
+    assert _q8(lib, x=None, N=0) == 0
+    assert _q8(lib, x8=None) == 1
+    assert _q8(lib, sc=FAKE + 2) == 4
+    assert _q8(lib, x8=FAKE + 8) == 4
+    assert _f8(lib, B=-1) == 2
+    assert _f8(lib, dtype=fa.FA_F32) == 3
+    assert _f8(lib, d=32) == 3
+    assert _f8(lib, q=None, N=0) == 0
+    assert _f8(lib, vs=None) == 1
+    assert _f8(lib, v=FAKE + 4) == 4
+    assert _f8(lib, ks=FAKE + 1) == 4
+    assert _f8(lib, scale=-1.0) == 5
+    # the padded V^T head must fit 32-bit byte offsets
+    assert _f8(lib, N=(1 << 24) - 1, d=128) == 2
+
+
+def test_fp8_valid_calls_without_gpu_stop_at_device_check(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; the device check passes")
+    assert _q8(lib) == 6
+    assert _q8(lib, transpose=1) == 6
+    assert _f8(lib) == 6
