@@ -237,7 +237,6 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const floa
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
     st = check_device();
     if (st != FA_OK) return st;
-    const bool eight = fa::fp8_eight_waves(B, H, N);
     fa::Fp8Args a;
     a.q8 = reinterpret_cast<const unsigned char*>(Q8);
     a.k8 = reinterpret_cast<const unsigned char*>(K8);
@@ -250,10 +249,10 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const floa
     a.n = (int)N;
     a.np = (int)fa::fp8_padded_len(N);
     a.nb = (int)fa::fp8_scale_blocks(N);
-    a.n_qblk = (int)fa::ceil_div(N, eight ? 256 : 128);
+    a.n_qblk = (int)fa::ceil_div(N, fa::kFp8BlockQ);
     a.n_blocks = (int)(B * H * a.n_qblk);
     a.c = (float)((double)scale * 1.4426950408889634074);
-    const int e = fa_launch_fwd_fp8(a, B * H, out_dtype, (int)d, eight ? 1 : 0, stream);
+    const int e = fa_launch_fwd_fp8(a, out_dtype, (int)d, stream);
     return e == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 

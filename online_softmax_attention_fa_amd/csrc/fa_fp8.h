@@ -42,15 +42,16 @@ struct Fp8Args {
     int n_blocks;
     float c;                   // scale * log2(e)
 };
-inline bool fp8_eight_waves(int64_t B, int64_t H, int64_t N) {
-    const int64_t g8 = B * H * ceil_div(N, 8 * 32);
-    return N >= 2048 && (g8 >= 2 * kCus || g8 % kCus == 0);
-}
+// Query rows per workgroup of the fp8 forward: 4 waves x 32 rows, two workgroups per CU.
+// (Measured at B=4 H=32 N=16384 d=128: 8% faster than one 8-wave workgroup per CU; the
+// two independent workgroups on a CU drift out of phase, so one's softmax overlaps the
+// other's MFMAs, where the waves of one workgroup meet at every tile's barrier.)
+constexpr int kFp8BlockQ = 128;
 
 }  // namespace fa
 
 // Launchers implemented in fa_fp8_kernel.hip (0 or the hipError_t of the launch).
 // in_dtype: input type of the quantiser; out_dtype: O's type in the forward.
 int fa_launch_quantize_fp8(const fa::QuantArgs& a, int64_t bh, int in_dtype, int d, int transpose, void* stream);
-int fa_launch_fwd_fp8(const fa::Fp8Args& a, int64_t bh, int out_dtype, int d, int eight_waves, void* stream);
+int fa_launch_fwd_fp8(const fa::Fp8Args& a, int out_dtype, int d, void* stream);
 

@@ -22,10 +22,10 @@
 //    query (B) -- dims 64s + 32(L/32) .. +31 for k-step s.
 //  * O^T += V^T P^T: the S^T accumulator leaves lane L with keys 8j + 4(L/32) + r
 //    (j, r < 4) of each 32-key block.  For a 64-key step, v_permlane32_swap trades the
-//    second block's codes of lanes 0-31 for the first block's of lanes 32-63, so lane L
-//    holds 32 keys 64s + 32(L/32) + {8j + r, then 8j + 4 + r}.  V is stored transposed
-//    (V^T, keys contiguous), so the A operand is two 16-byte LDS reads of 32 consecutive
-//    keys whose dwords are then taken in the order 0, 2, 4, 6, 1, 3, 5, 7 to match.
+//    second block's codes of lanes 0-31 for the first block's of lanes 32-63; taking the
+//    swapped pair of registers as dwords 2j and 2j + 1 gives lane L the 32 keys
+//    64s + 32(L/32) + 0 .. 31 in order.  V is stored transposed (V^T, keys contiguous), so
+//    the A operand is two plain 16-byte LDS reads of the same 32 keys.
 
 #include "fa_device.h"
 #include "fa_fp8.h"
@@ -201,9 +201,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_fp8_kernel
     const unsigned char* __restrict__ Qh = a.q8 + (int64_t)bh * N * D;
     const unsigned char* __restrict__ Kh = a.k8 + (int64_t)bh * N * D;
     const unsigned char* __restrict__ Vh = a.vt8 + (int64_t)bh * D * NP;
-    const float* __restrict__ qsh = a.qs + (int64_t)bh * NB;
-    const float* __restrict__ ksh = a.ks + (int64_t)bh * NB;
-    const float* __restrict__ vsh = a.vs + (int64_t)bh * NB;
+    // Scale tables are read-only for the kernel's lifetime: read them through the constant
+    // address space, i.e. with scalar loads.  (Vector loads would be counted with the
+    // tile copies in flight, and waiting for a scale would then wait for the next tile.)
+    typedef __attribute__((address_space(4))) const float cfloat;
+    const cfloat* qsh = (const cfloat*)(a.qs + (int64_t)bh * NB);
+    const cfloat* ksh = (const cfloat*)(a.ks + (int64_t)bh * NB);
+    const cfloat* vsh = (const cfloat*)(a.vs + (int64_t)bh * NB);
     TO* __restrict__ Oh = reinterpret_cast<TO*>(a.o) + (int64_t)bh * N * D;
     float* __restrict__ Lh = a.lse + (int64_t)bh * N;
 
@@ -317,33 +321,31 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_fp8_kernel
                 }
         }
 
-        unsigned pk[KB][4];
-        float tsum;
-        auto make_p = [&](float neg_m) {
-            tsum = 0.f;
+        // P, its sums and O^T += V^T P^T one 64-key step at a time: the softmax of a step
+        // overlaps the score MFMAs still running for the next step and the P V MFMAs of the
+        // previous one.  Each step is its own online-softmax block: it is redone with its
+        // own maximum when a lane's sum of P over it leaves range.
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
+            unsigned pk[2][4];
+            float tsum;
+            auto make_p = [&](float neg_m) {
                 const float nm = neg_m + vsh_e[ks];
                 float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const int kb = 2 * ks + kk;
                     float p[16];
 #pragma unroll
-                    for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(s[kb][t], ck[ks], nm));
+                    for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(s[2 * ks + kk][t], ck[ks], nm));
 #pragma unroll
                     for (int t = 0; t < 16; t += 2) { acc0 += p[t]; acc1 += p[t + 1]; }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) pk[kb][q] = pack4_fp8(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
+                    for (int q = 0; q < 4; ++q) pk[kk][q] = pack4_fp8(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
                 }
-                tsum = __builtin_fmaf(acc0 + acc1, vw[ks], tsum);
-            }
-        };
-        make_p(-m);
-        if (__builtin_amdgcn_ballot_w64(!(tsum <= kFp8MaxTileSum)) != 0) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+                tsum = (acc0 + acc1) * vw[ks];
+            };
+            make_p(-m);
+            if (__builtin_amdgcn_ballot_w64(!(tsum <= kFp8MaxTileSum)) != 0) {
                 float x0 = -INFINITY, x1 = -INFINITY;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
@@ -352,41 +354,40 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_fp8_kernel
                         x0 = vmax3(x0, s[2 * ks + kk][t], s[2 * ks + kk][t + 1]);
                         x1 = vmax3(x1, s[2 * ks + kk][t + 2], s[2 * ks + kk][t + 3]);
                     }
-                mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(x0, x1) * ck[ks]);
+                const float mx = pair_max(__builtin_elementwise_maximum(x0, x1) * ck[ks]);
+                const float mnew = fmaxf(m, mx);
+                const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+                m = mnew;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) o[db][t] *= alpha;
+                make_p(-m);
             }
-            mx = pair_max(mx);
-            const float mnew = fmaxf(m, mx);
-            const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
-            m = mnew;
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int t = 0; t < 16; ++t) o[db][t] *= alpha;
-            make_p(-m);
-        }
-        lsum += tsum;
+            lsum += tsum;
 
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            unsigned bx[4], by[4];
+            __builtin_amdgcn_s_setprio(1);
+            // lanes 0-31 keep block 2ks's codes and take block 2ks+1's from lanes 32-63
+            // (and the reverse), interleaved so that dword i holds keys 4i .. 4i+3 of the
+            // lane's 32, the order of V^T in LDS
+            unsigned pbw[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const auto r = __builtin_amdgcn_permlane32_swap(pk[2 * ks][q], pk[2 * ks + 1][q], false, false);
-                bx[q] = r[0];
-                by[q] = r[1];
+                const auto r = __builtin_amdgcn_permlane32_swap(pk[0][q], pk[1][q], false, false);
+                pbw[2 * q] = r[0];
+                pbw[2 * q + 1] = r[1];
             }
-            const i32x8 pb = {(int)bx[0], (int)bx[1], (int)bx[2], (int)bx[3], (int)by[0], (int)by[1], (int)by[2], (int)by[3]};
+            const i32x8 pb = {(int)pbw[0], (int)pbw[1], (int)pbw[2], (int)pbw[3], (int)pbw[4], (int)pbw[5], (int)pbw[6], (int)pbw[7]};
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const u32x4 n0 = lds_read16(sbase, voff[ks][0] + db * 32 * RV);
                 const u32x4 n1 = lds_read16(sbase, voff[ks][1] + db * 32 * RV);
-                const i32x8 va = {(int)n0[0], (int)n0[2], (int)n1[0], (int)n1[2], (int)n0[1], (int)n0[3], (int)n1[1], (int)n1[3]};
+                const i32x8 va = {(int)n0[0], (int)n0[1], (int)n0[2], (int)n0[3], (int)n1[0], (int)n1[1], (int)n1[2], (int)n1[3]};
                 o[db] = mma_fp8(va, pb, o[db]);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
-        __builtin_amdgcn_s_setprio(0);
     };
 
     issue_tile(0, stage0);
@@ -434,11 +435,9 @@ int launch_quant_t(const QuantArgs& a, int64_t bh, int transpose, void* stream) 
 }
 
 template <typename TO, int D>
-int launch_fp8_t(const Fp8Args& a, int eight, void* stream) {
-    if (eight)
-        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, 8>), dim3(a.n_blocks), dim3(512), 0, (hipStream_t)stream, a);
-    else
-        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, 4>), dim3(a.n_blocks), dim3(256), 0, (hipStream_t)stream, a);
+int launch_fp8_t(const Fp8Args& a, void* stream) {
+    constexpr int WAVES = kFp8BlockQ / 32;
+    hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, WAVES>), dim3(a.n_blocks), dim3(64 * WAVES), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 
@@ -452,11 +451,8 @@ int fa_launch_quantize_fp8(const fa::QuantArgs& a, int64_t bh, int in_dtype, int
                     : fa::launch_quant_t<_Float16, 64>(a, bh, transpose, stream);
 }
 
-int fa_launch_fwd_fp8(const fa::Fp8Args& a, int64_t bh, int out_dtype, int d, int eight_waves, void* stream) {
-    (void)bh;
+int fa_launch_fwd_fp8(const fa::Fp8Args& a, int out_dtype, int d, void* stream) {
     if (out_dtype == FA_BF16)
-        return d == 128 ? fa::launch_fp8_t<__bf16, 128>(a, eight_waves, stream)
-                        : fa::launch_fp8_t<__bf16, 64>(a, eight_waves, stream);
-    return d == 128 ? fa::launch_fp8_t<_Float16, 128>(a, eight_waves, stream)
-                    : fa::launch_fp8_t<_Float16, 64>(a, eight_waves, stream);
+        return d == 128 ? fa::launch_fp8_t<__bf16, 128>(a, stream) : fa::launch_fp8_t<__bf16, 64>(a, stream);
+    return d == 128 ? fa::launch_fp8_t<_Float16, 128>(a, stream) : fa::launch_fp8_t<_Float16, 64>(a, stream);
 }

@@ -166,8 +166,7 @@ def test_fp8_edge_workload_closed_forms(gpu_lib):
 
 @pytest.mark.parametrize("B,H,N", [(4, 16, 2049), (4, 32, 16384)])
 def test_fp8_large_sampled(gpu_lib, B, H, N):
-    """The 8-wave plan (B*H*ceil(N/256) >= 512), launched as the benchmark launches it, on
-    sampled rows of three heads."""
+    """Large grids, launched as the benchmark launches them, on sampled rows of three heads."""
     import torch
 
     d = 128
