@@ -58,10 +58,15 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the forward kernel's sources with comments and blank space removed, so that
+    an edit to a comment does not invalidate the recorded counters."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

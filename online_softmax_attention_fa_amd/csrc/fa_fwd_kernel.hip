@@ -20,14 +20,16 @@
 //    plus one exchange with lane L^32 (v_permlane32_swap).
 //  * The probabilities P^T are used straight from those accumulator registers as the
 //    B operand of O^T += V^T P^T (after packing to bf16/fp16): the MFMA's contraction
-//    index is permuted, and V^T is stored in LDS in the same permuted key order so the
-//    A operand is one 16-byte LDS read per lane.  No LDS round trip for P.
+//    index is permuted to the keys each lane holds, and the A operand (V^T) is gathered
+//    from row-major V in LDS in the same key order by two transposing LDS reads
+//    (ds_read_b64_tr_b16).  No LDS round trip for P.
 //  * O^T's accumulator also has one query per lane, so the per-row rescale is a
 //    multiply by a per-lane scalar.
-//  * The maximum used for the exponent is only moved when a tile's maximum exceeds it
-//    by more than 2^8 (base-2 units); exact softmax does not depend on that choice
-//    (the same m is used for l, O and LSE), P stays <= 256, and the O rescale runs
-//    only on the few tiles where the maximum jumps.
+//  * P is formed with the running maximum m as it stands; no per-tile row maximum is
+//    taken.  Exact softmax does not depend on m (the same m is used for l, O and LSE),
+//    which only has to keep P finite and in range: a tile is redone with its own maximum,
+//    and O and l rescaled, only when a row's sum of P over the tile leaves [0, 2^15] --
+//    the first tile (m = -inf) or a maximum that jumped.
 //  * LDS tiles use an XOR swizzle of 16-byte chunks so the 16 lanes that read one
 //    chunk column of consecutive rows hit distinct banks.
 //  * Workgroup ids are remapped so consecutive query blocks of one head land on the
