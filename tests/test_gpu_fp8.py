@@ -126,12 +126,13 @@ def _check_head(O, L, q, k, v, scale, out_dtype, rows, what):
 @pytest.mark.parametrize("out_dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 63, 65, 129, 300, 1000])
-def test_fp8_forward_parity(gpu_lib, out_dtype, d, N):
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp16"])
+def test_fp8_forward_parity(gpu_lib, in_dtype, out_dtype, d, N):
     B, H = 1, 3
-    q, k, v = (wl.random_tensor((B, H, N, d), "bf16", [N, d, t]) for t in (1, 2, 3))
+    q, k, v = (wl.random_tensor((B, H, N, d), in_dtype, [N, d, t]) for t in (1, 2, 3))
     v[0, 1, : min(N, 40)] *= 16.0          # V blocks of different scales within one head
-    v = wl.round_to_dtype(v, "bf16")
-    O, L = _run_fp8(gpu_lib, q, k, v, "bf16", out_dtype)
+    v = wl.round_to_dtype(v, in_dtype)
+    O, L = _run_fp8(gpu_lib, q, k, v, in_dtype, out_dtype)
     worst = 0.0
     for h in range(H):
         e, frac, le = _check_head(O[0, h], L[0, h], q[0, h], k[0, h], v[0, h], scale_of(d), out_dtype,
