@@ -229,14 +229,23 @@ def sweep(fa, stream, steps=20):
         ("bf16 B1 H1 N16384 d128 split-KV", 1, 1, 16384, 128, torch.bfloat16, "split"),
         ("bf16 B1 H8 N4096 d128", 1, 8, 4096, 128, torch.bfloat16, "plain"),
         ("bf16 B1 H8 N4096 d128 split-KV", 1, 8, 4096, 128, torch.bfloat16, "split"),
-    ] + [(f"bf16 B16 H64 N{n} d128", 16, 64, n, 128, torch.bfloat16, "plain") for n in (128, 256, 512)]
+    ] + [(f"bf16 B16 H64 N{n} d128", 16, 64, n, 128, torch.bfloat16, "plain") for n in (128, 256, 512)] + [
+        ("bf16 B8 H32 decode Nq1 Nk16384 d128 split-KV", 8, 32, 16384, 128, torch.bfloat16, "decode"),
+    ]
     rows = []
     for name, b, h, n, d, dt, mode in cases:
-        q, k, v = (torch.randn(b, h, n, d, device=dev, dtype=dt, generator=gen) for _ in range(3))
+        nq = 1 if mode == "decode" else n
+        q = torch.randn(b, h, nq, d, device=dev, dtype=dt, generator=gen)
+        k, v = (torch.randn(b, h, n, d, device=dev, dtype=dt, generator=gen) for _ in range(2))
         o = torch.empty_like(q)
-        lse = torch.empty(b, h, n, device=dev, dtype=torch.float32)
+        lse = torch.empty(b, h, nq, device=dev, dtype=torch.float32)
         sc = 1.0 / math.sqrt(d)
-        if mode == "split":
+        if mode == "decode":
+            splits = fa.fa_fwd_splitkv_qk_splits(b, h, nq, n, d, dt)
+            ws = torch.empty(max(1, fa.fa_fwd_splitkv_qk_workspace_bytes(b, h, nq, n, d, dt, splits)),
+                             dtype=torch.uint8, device=dev)
+            fn = lambda: fa.fa_fwd_splitkv(q, k, v, o, lse, splits=splits, workspace=ws, scale=sc, stream=stream)
+        elif mode == "split":
             splits = fa.fa_fwd_splitkv_splits(b, h, n, d, dt)
             ws = torch.empty(max(1, fa.fa_fwd_splitkv_workspace_bytes(b, h, n, d, dt, splits)),
                              dtype=torch.uint8, device=dev)
@@ -245,14 +254,14 @@ def sweep(fa, stream, steps=20):
             fn = lambda: fa.fa_fwd(q, k, v, o, lse, scale=sc, stream=stream, causal=(mode == "causal"))
         t = launch_times(fn, stream, steps)
         tmin, tmed = min(t), statistics.median(t)
-        flops = 4.0 * b * h * n * n * d * (0.5 if mode == "causal" else 1.0)
-        nbytes = 4.0 * b * h * n * d * q.element_size() + 4.0 * b * h * n
+        flops = 4.0 * b * h * nq * n * d * (0.5 if mode == "causal" else 1.0)
+        nbytes = (2.0 * nq + 2.0 * n) * b * h * d * q.element_size() + 4.0 * b * h * nq
         peak = 157.3 if dt == torch.float32 else PEAK_BF16_TFLOPS
         r = {"case": name, "min_ms": round(tmin, 4), "median_ms": round(tmed, 4),
              "tflops": round(flops / (tmed * 1e-3) / 1e12, 2),
              "pct_of_mfma_peak": round(100 * flops / (tmed * 1e-3) / 1e12 / peak, 2),
              "gbps": round(nbytes / (tmed * 1e-3) / 1e9, 1)}
-        if mode == "split":
+        if mode in ("split", "decode"):
             r["splits"] = splits
         rows.append(r)
         log(f"sweep {name}: median {tmed * 1e3:.1f} us, min {tmin * 1e3:.1f} us, {r['tflops']} TFLOP/s "

@@ -129,6 +129,22 @@ fa_status fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, f
                          float scale, fa_dtype dtype, int32_t splits, void* stream);
 
 /*
+ * The same with Nq query rows and Nk keys per head (Q, O [B,H,Nq,d]; K, V [B,H,Nk,d]; LSE
+ * [B,H,Nq]): every query attends to all Nk keys -- a chunk of new queries against a longer
+ * key/value history, or one query per head when decoding.  It is the split-KV forward
+ * above with the two lengths apart (fa_fwd_splitkv is this call with Nq = Nk = N); the
+ * split count and workspace refer to Nk's key tiles and Nq's rows.  Nq > 0 with Nk = 0 is
+ * FA_ERR_SHAPE (no keys to attend to); Nq = 0 is an empty problem.
+ */
+size_t fa_fwd_splitkv_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                         fa_dtype dtype, int32_t splits);
+int32_t fa_fwd_splitkv_qk_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, fa_dtype dtype);
+fa_status fa_fwd_splitkv_qk(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            void* workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
+                            int64_t Nk, int64_t d, float scale, fa_dtype dtype, int32_t splits,
+                            void* stream);
+
+/*
  * Workspace the backward needs, in bytes: two fp32 values per row (B*H*N rows).
  * Returns 0 for invalid or empty shapes.
  */

@@ -25,7 +25,8 @@ STATUS = {
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_causal", "fa_fwd_plan", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_splits",
-           "fa_fwd_splitkv", "fa_fp8_padded_len", "fa_fp8_scale_blocks", "fa_quantize_fp8", "fa_fwd_fp8",
+           "fa_fwd_splitkv", "fa_fwd_splitkv_qk_workspace_bytes", "fa_fwd_splitkv_qk_splits", "fa_fwd_splitkv_qk",
+           "fa_fp8_padded_len", "fa_fp8_scale_blocks", "fa_quantize_fp8", "fa_fwd_fp8",
            "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal", "fa_status_str", "fa_version")
 
 
@@ -71,6 +72,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_splitkv_splits.restype = ctypes.c_int32
     lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, P, ctypes.c_size_t, I64, I64, I64, I64, F, I, ctypes.c_int32, P]
     lib.fa_fwd_splitkv.restype = I
+    lib.fa_fwd_splitkv_qk_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I, ctypes.c_int32]
+    lib.fa_fwd_splitkv_qk_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_splitkv_qk_splits.argtypes = [I64, I64, I64, I64, I64, I]
+    lib.fa_fwd_splitkv_qk_splits.restype = ctypes.c_int32
+    lib.fa_fwd_splitkv_qk.argtypes = [P, P, P, P, P, P, ctypes.c_size_t, I64, I64, I64, I64, I64, F, I,
+                                      ctypes.c_int32, P]
+    lib.fa_fwd_splitkv_qk.restype = I
     lib.fa_fp8_padded_len.argtypes = [I64]
     lib.fa_fp8_padded_len.restype = I64
     lib.fa_fp8_scale_blocks.argtypes = [I64]
@@ -182,12 +190,29 @@ def fa_fwd_splitkv_splits(B, H, N, d, dtype) -> int:
     return int(load().fa_fwd_splitkv_splits(B, H, N, d, code))
 
 
+def fa_fwd_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, dtype, splits=0) -> int:
+    """Workspace bytes of ``fa_fwd_splitkv_qk`` (Nq query rows, Nk keys per head)."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(load().fa_fwd_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, code, splits))
+
+
+def fa_fwd_splitkv_qk_splits(B, H, Nq, Nk, d, dtype) -> int:
+    """The split count ``fa_fwd_splitkv_qk`` picks for ``splits=0``."""
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(load().fa_fwd_splitkv_qk_splits(B, H, Nq, Nk, d, code))
+
+
 def fa_fwd_splitkv(q, k, v, o=None, lse=None, splits=0, workspace=None, scale=None, stream=None):
     """O, LSE = attention(q, k, v) with the key range cut into ``splits`` parts that are
-    computed separately and merged by their LSE (``fa_fwd_splitkv``).  Returns (o, lse)."""
+    computed separately and merged by their LSE.  q [B, H, Nq, d]; k, v [B, H, Nk, d]:
+    ``fa_fwd_splitkv`` when Nq = Nk, ``fa_fwd_splitkv_qk`` otherwise.  Returns (o, lse)."""
     import torch
 
     lib = load()
+    if k.dim() != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"k must be [B, H, Nk, d] with q's B, H, d: q {tuple(q.shape)} k {tuple(k.shape)}")
+    if k.shape[2] != q.shape[2]:
+        return _splitkv_qk(lib, q, k, v, o, lse, splits, workspace, scale, stream)
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     if scale is None:
@@ -273,6 +298,36 @@ def fa_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, o=None, lse=None, scale=N
                             v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
                             dtype_code(out_dtype), _stream_handle(stream))
     _check(st, "fa_fwd_fp8")
+    return o, lse
+
+
+def _splitkv_qk(lib, q, k, v, o, lse, splits, workspace, scale, stream):
+    import torch
+
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous device tensor of q's dtype")
+    if v.shape != k.shape:
+        raise ValueError("v must have k's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
+        raise ValueError("o must be contiguous, shaped and typed like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, Nq]")
+    code = dtype_code(q.dtype)
+    need = int(lib.fa_fwd_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, code, splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_splitkv_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel(), B, H, Nq, Nk, d, float(scale), code,
+                                   int(splits), _stream_handle(stream))
+    _check(st, "fa_fwd_splitkv_qk")
     return o, lse
 
 

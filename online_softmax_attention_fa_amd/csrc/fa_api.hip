@@ -54,9 +54,12 @@ fa_status check_problem(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
     return FA_OK;
 }
 
+// Nk keys per head for N query rows (Nk = N except in a split-KV call with unequal lengths;
+// already validated there).
 fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float* LSE,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
-                     void* stream, int causal) {
+                     void* stream, int causal, int64_t Nk = -1) {
+    if (Nk < 0) Nk = N;
     fa_status st = check_problem(B, H, N, d, dtype);
     if (st != FA_OK) return st;
     if (B * H * N == 0) return FA_OK;   // empty tensors may carry NULL data pointers
@@ -75,6 +78,7 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
     a.o = O;
     a.lse = LSE;
     a.n = (int)N;
+    a.nk = (int)Nk;
     a.n_qblk = (int)fa::ceil_div(N, plan.block_q);
     a.n_blocks = (int)plan.grid;
     a.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
@@ -86,22 +90,39 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
     return e == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 
-fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, float* LSE, void* ws,
-                         size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                         fa_dtype dtype, int32_t splits, void* stream) {
+// Shapes of a split-KV call: N query rows and Nk keys per head, both within the 32-bit
+// index math; queries with no keys to attend to are a shape error.
+fa_status check_splitkv(int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d, int dtype, int32_t splits) {
     fa_status st = check_problem(B, H, N, d, dtype);
+    if (st != FA_OK) return st;
+    st = check_problem(B, H, Nk, d, dtype);
     if (st != FA_OK) return st;
     if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
     if (splits < 0 || splits > fa::kMaxKvSplits) return FA_ERR_SHAPE;
+    if (B * H * N > 0 && Nk == 0) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+// The split count a call will use: splits = 0 picks, more than the key tiles is clamped.
+int32_t effective_splits(int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d, int32_t splits) {
+    if (splits == 0) splits = fa::choose_kv_splits(B, H, N, Nk, d);
+    const int64_t tiles = fa::ceil_div(Nk, fa::splitkv_block_k(d));
+    return splits > tiles ? (int32_t)tiles : splits;
+}
+
+fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, float* LSE, void* ws,
+                         size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d, float scale,
+                         fa_dtype dtype, int32_t splits, void* stream) {
+    fa_status st = check_splitkv(B, H, N, Nk, d, dtype, splits);
+    if (st != FA_OK) return st;
     if (B * H * N == 0) return FA_OK;
     if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
         return FA_ERR_ALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
-    if (splits == 0) splits = fa::choose_kv_splits(B, H, N, d);
-    const int64_t tiles = fa::ceil_div(N, fa::splitkv_block_k(d));
-    if (splits > tiles) splits = (int32_t)tiles;
-    if (splits <= 1) return fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, dtype, stream, 0);
+    splits = effective_splits(B, H, N, Nk, d, splits);
+    const int64_t tiles = fa::ceil_div(Nk, fa::splitkv_block_k(d));
+    if (splits <= 1) return fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, dtype, stream, 0, Nk);
     const size_t need = fa::splitkv_workspace_bytes(B, H, N, d, splits);
     if (!ws || !aligned(ws, 256) || ws_bytes < need) return FA_ERR_WORKSPACE;
     st = check_device();
@@ -114,6 +135,7 @@ fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, f
     a.o = O;
     a.lse = LSE;
     a.n = (int)N;
+    a.nk = (int)Nk;
     a.n_qblk = (int)fa::ceil_div(N, 128);
     a.splits = splits;
     a.tiles_per_split = (int)fa::ceil_div(tiles, splits);
@@ -178,24 +200,35 @@ fa_status bwd_common(const void* Q, const void* K, const void* V, const void* O,
 
 extern "C" {
 
+size_t fa_fwd_splitkv_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, fa_dtype dtype,
+                                         int32_t splits) {
+    if (check_splitkv(B, H, Nq, Nk, d, dtype, splits) != FA_OK || B * H * Nq == 0) return 0;
+    return fa::splitkv_workspace_bytes(B, H, Nq, d, effective_splits(B, H, Nq, Nk, d, splits));
+}
+
+int32_t fa_fwd_splitkv_qk_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, fa_dtype dtype) {
+    if (check_splitkv(B, H, Nq, Nk, d, dtype, 0) != FA_OK || B * H * Nq == 0) return 1;
+    return fa::choose_kv_splits(B, H, Nq, Nk, d);
+}
+
+fa_status fa_fwd_splitkv_qk(const void* Q, const void* K, const void* V, void* O, float* LSE, void* workspace,
+                            size_t ws_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                            fa_dtype dtype, int32_t splits, void* stream) {
+    return splitkv_common(Q, K, V, O, LSE, workspace, ws_bytes, B, H, Nq, Nk, d, scale, dtype, splits, stream);
+}
+
 size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype, int32_t splits) {
-    if (check_problem(B, H, N, d, dtype) != FA_OK || dtype == FA_F32) return 0;
-    if (splits < 0 || splits > fa::kMaxKvSplits || B * H * N == 0) return 0;
-    if (splits == 0) splits = fa::choose_kv_splits(B, H, N, d);
-    const int64_t tiles = fa::ceil_div(N, fa::splitkv_block_k(d));
-    if (splits > tiles) splits = (int32_t)tiles;
-    return fa::splitkv_workspace_bytes(B, H, N, d, splits);
+    return fa_fwd_splitkv_qk_workspace_bytes(B, H, N, N, d, dtype, splits);
 }
 
 int32_t fa_fwd_splitkv_splits(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype) {
-    if (check_problem(B, H, N, d, dtype) != FA_OK || dtype == FA_F32 || B * H * N == 0) return 1;
-    return fa::choose_kv_splits(B, H, N, d);
+    return fa_fwd_splitkv_qk_splits(B, H, N, N, d, dtype);
 }
 
 fa_status fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, void* workspace,
                          size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
                          int32_t splits, void* stream) {
-    return splitkv_common(Q, K, V, O, LSE, workspace, ws_bytes, B, H, N, d, scale, dtype, splits, stream);
+    return splitkv_common(Q, K, V, O, LSE, workspace, ws_bytes, B, H, N, N, d, scale, dtype, splits, stream);
 }
 
 int64_t fa_fp8_padded_len(int64_t N) { return N < 0 ? 0 : fa::fp8_padded_len(N); }

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
     const int h = lane >> 5, l32 = lane & 31;
-    const int N = a.n;
+    const int N = a.n, NK = a.nk;   // query rows, keys (equal unless a split-KV call differs)
 
     const int bid = remap_xcd(blockIdx.x, a.n_blocks);
     // split-KV: the splits of one query block are neighbours in the grid (same XCD, L2)
@@ -94,10 +94,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
     int qblk = rem / nsplit;
     const int split = rem - qblk * nsplit;
     if (CAUSAL) qblk = a.n_qblk - 1 - qblk;   // longest rows first
-    const int64_t head = (int64_t)bh * N * D;
+    const int64_t head = (int64_t)bh * N * D, khead = (int64_t)bh * NK * D;
     const T* __restrict__ Qh = reinterpret_cast<const T*>(a.q) + head;
-    const T* __restrict__ Kh = reinterpret_cast<const T*>(a.k) + head;
-    const T* __restrict__ Vh = reinterpret_cast<const T*>(a.v) + head;
+    const T* __restrict__ Kh = reinterpret_cast<const T*>(a.k) + khead;
+    const T* __restrict__ Vh = reinterpret_cast<const T*>(a.v) + khead;
     T* __restrict__ Oh = reinterpret_cast<T*>(a.o) + head;
     float* __restrict__ Lh = a.lse + (int64_t)bh * N;
 
@@ -132,13 +132,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
     }
 
     // ---- direct HBM -> LDS copy of tile j into a stage, through buffer resources that
-    // cover exactly this head's K (V): reads past row N - 1 return zeros, so the ragged
+    // cover exactly this head's K (V): reads past row NK - 1 return zeros, so the ragged
     // last tile needs no special case (its padded keys are also masked to -inf).
     // Wave w, copy i fills the 1 KiB block i*4 + w of the tile; lane L's 16 bytes land
     // at block + 16 L, i.e. row `row`, swizzled chunk `ch`.  The tile offset is added to
     // the per-lane (VGPR) offset, not passed as the scalar offset, so the buffer's range
     // check sees the full byte offset whichever of the two it covers.
-    const int head_bytes = N * D * 2;
+    const int head_bytes = NK * D * 2;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, head_bytes, kBufferRsrcWord3);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, head_bytes, kBufferRsrcWord3);
     int src_off[LOADS];
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
         for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
     float m = -INFINITY, lsum = 0.f, lrnd = 0.f;
 
-    int n_tiles = (N + BC - 1) / BC;
+    int n_tiles = (NK + BC - 1) / BC;
     if (CAUSAL) n_tiles = min(n_tiles, (min(N, (qblk + 1) * BR) + BC - 1) / BC);
     int t0 = 0;   // first key tile of this workgroup
     if (SPLIT) {
@@ -203,8 +203,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
         }
 
         __builtin_amdgcn_s_setprio(0);
-        // ---- masks: keys past N (tail tile), keys after the query (causal)
-        const bool tail = kbase + BC > N;
+        // ---- masks: keys past NK (tail tile), keys after the query (causal)
+        const bool tail = kbase + BC > NK;
         const bool diag = CAUSAL && (kbase + BC - 1 > q_wave);
         if (tail || diag) {
 #pragma unroll
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(Fwd
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
                     const int key = kbase + kb * 32 + 8 * (t >> 2) + 4 * h + (t & 3);
-                    bool drop = key >= N;
+                    bool drop = key >= NK;
                     if (CAUSAL) drop = drop || key > query;
                     if (drop) s[kb][t] = -INFINITY;
                 }

@@ -19,8 +19,9 @@ struct FwdArgs {
     const void* v;
     void* o;
     float* lse;
-    int n;          // sequence length N
-    int n_qblk;     // ceil(N / Br)
+    int n;          // query rows per head (N, or Nq when queries and keys differ in length)
+    int nk;         // keys per head (= n for self-attention)
+    int n_qblk;     // ceil(n / Br)
     int n_blocks;   // workgroups in the grid = B*H*n_qblk (*splits)
     float c;        // scale * log2(e): scores are taken to base 2 inside the kernel
     // split-KV only: key tiles [s*tiles_per_split, (s+1)*tiles_per_split) per split s;
@@ -128,9 +129,9 @@ inline size_t splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d
 }
 // The chooser's split count: enough workgroups for two per CU, each split at least two
 // key tiles; 1 when the plain grid already fills the chip.
-inline int choose_kv_splits(int64_t B, int64_t H, int64_t N, int64_t d) {
-    const int64_t grid = B * H * ceil_div(N, 128);
-    const int64_t tiles = ceil_div(N, splitkv_block_k(d));
+inline int choose_kv_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+    const int64_t grid = B * H * ceil_div(Nq, 128);
+    const int64_t tiles = ceil_div(Nk, splitkv_block_k(d));
     if (grid >= 2 * kCus) return 1;
     int64_t s = ceil_div(2 * kCus, grid);
     if (s > tiles / 2) s = tiles / 2;

@@ -284,3 +284,39 @@ def test_fp8_valid_calls_without_gpu_stop_at_device_check(lib):
     assert _q8(lib) == 6
     assert _q8(lib, transpose=1) == 6
     assert _f8(lib) == 6
+
+
+def _skv_qk(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=WS, ws_bytes=1 << 40, B=2, H=4, Nq=1, Nk=5000,
+            d=128, scale=0.125, dtype=fa.FA_BF16, splits=0):
+    return lib.fa_fwd_splitkv_qk(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, d, scale, dtype, splits, None)
+
+
+def test_splitkv_qk_sizes_and_validation(lib):
+    # the square case is the same call
+    assert lib.fa_fwd_splitkv_qk_workspace_bytes(2, 3, 1000, 1000, 64, fa.FA_BF16, 4) == \
+        lib.fa_fwd_splitkv_workspace_bytes(2, 3, 1000, 64, fa.FA_BF16, 4)
+    assert lib.fa_fwd_splitkv_qk_splits(1, 1, 16384, 16384, 128, fa.FA_BF16) == \
+        lib.fa_fwd_splitkv_splits(1, 1, 16384, 128, fa.FA_BF16)
+    # decode: rows are Nq's, splits follow Nk's key tiles (5000 keys / 64 = 79 tiles)
+    s = lib.fa_fwd_splitkv_qk_splits(2, 4, 1, 5000, 128, fa.FA_BF16)
+    assert 2 <= s <= 39
+    rows = 2 * 4 * 1
+    assert lib.fa_fwd_splitkv_qk_workspace_bytes(2, 4, 1, 5000, 128, fa.FA_BF16, 8) == \
+        -(-8 * rows * 128 * 4 // 256) * 256 + -(-8 * rows * 4 // 256) * 256
+    assert lib.fa_fwd_splitkv_qk_workspace_bytes(2, 4, 1, 100, 128, fa.FA_BF16, 64) == \
+        lib.fa_fwd_splitkv_qk_workspace_bytes(2, 4, 1, 100, 128, fa.FA_BF16, 2)   # 2 key tiles
+    assert _skv_qk(lib, Nk=0) == 2            # queries with no keys
+    assert _skv_qk(lib, Nq=0, Nk=0, q=None) == 0
+    assert _skv_qk(lib, Nq=-1) == 2
+    assert _skv_qk(lib, Nk=-5) == 2
+    assert _skv_qk(lib, dtype=fa.FA_F32) == 3
+    assert _skv_qk(lib, k=None) == 1
+    assert _skv_qk(lib, ws=None, splits=8) == 8
+
+
+def test_splitkv_qk_without_gpu_stops_at_device_check(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; the device check passes")
+    assert _skv_qk(lib, splits=8) == 6

@@ -101,3 +101,23 @@ def test_splitkv_long_single_head_sampled(gpu_lib):
     t_plain = timed(lambda: gpu_lib.fa_fwd(tq, tk, tv, o, lse))
     t_split = timed(lambda: gpu_lib.fa_fwd_splitkv(tq, tk, tv, o, lse, workspace=ws))
     print(f"B=1 H=1 N={N}: plain {t_plain:.3f} ms, split-KV x{splits} {t_split:.3f} ms")
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,dtype,splits", [
+    (2, 4, 1, 5000, 128, "bf16", 0),      # decode: one query per head
+    (1, 3, 1, 777, 64, "fp16", 5),
+    (1, 2, 7, 3000, 128, "fp16", 0),      # a few new queries against a long history
+    (2, 2, 300, 100, 128, "bf16", 1),     # more queries than keys, no split
+    (1, 2, 130, 4097, 64, "bf16", 9),
+])
+def test_splitkv_unequal_lengths(gpu_lib, B, H, Nq, Nk, d, dtype, splits):
+    import torch
+
+    q = wl.random_tensor((B, H, Nq, d), dtype, [Nq, Nk, 1])
+    k = wl.random_tensor((B, H, Nk, d), dtype, [Nq, Nk, 2])
+    v = wl.random_tensor((B, H, Nk, d), dtype, [Nq, Nk, 3])
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    o, lse = gpu_lib.fa_fwd_splitkv(tq, tk, tv, splits=splits)
+    torch.cuda.synchronize()
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(d))
+    compare(to_host(o), lse.cpu().numpy().astype(np.float64), O_ref, L_ref, dtype, f"Nq={Nq} Nk={Nk} splits={splits}")
