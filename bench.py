@@ -212,7 +212,8 @@ def launch_times(fn, stream, steps, warmup=5):
 
 
 def sweep(fa, stream, steps=20):
-    """Forward timings of the smaller workloads and the bandwidth-bound short sequences."""
+    """Forward timings of the smaller workloads, the bandwidth-bound short sequences, a decode
+    shape, and one small call replayed from a captured graph."""
     import statistics
 
     import torch
@@ -221,6 +222,7 @@ def sweep(fa, stream, steps=20):
     gen = torch.Generator(device=dev).manual_seed(7)
     cases = [
         ("fp32 B1 H1 N256 d64", 1, 1, 256, 64, torch.float32, "plain"),
+        ("fp32 B1 H1 N256 d64 graph replay", 1, 1, 256, 64, torch.float32, "graph"),
         ("bf16 B4 H16 N2048 d64", 4, 16, 2048, 64, torch.bfloat16, "plain"),
         ("fp16 B1 H32 N16384 d128", 1, 32, 16384, 128, torch.float16, "plain"),
         ("bf16 B2 H8 N4097 d128", 2, 8, 4097, 128, torch.bfloat16, "plain"),
@@ -245,6 +247,18 @@ def sweep(fa, stream, steps=20):
             ws = torch.empty(max(1, fa.fa_fwd_splitkv_qk_workspace_bytes(b, h, nq, n, d, dt, splits)),
                              dtype=torch.uint8, device=dev)
             fn = lambda: fa.fa_fwd_splitkv(q, k, v, o, lse, splits=splits, workspace=ws, scale=sc, stream=stream)
+        elif mode == "graph":
+            # the call captured once in a HIP graph and replayed: no per-call launch work
+            s2 = torch.cuda.Stream()
+            s2.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s2):
+                fa.fa_fwd(q, k, v, o, lse, scale=sc)
+            torch.cuda.current_stream().wait_stream(s2)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fa.fa_fwd(q, k, v, o, lse, scale=sc)
+            fn = graph.replay
         elif mode == "split":
             splits = fa.fa_fwd_splitkv_splits(b, h, n, d, dt)
             ws = torch.empty(max(1, fa.fa_fwd_splitkv_workspace_bytes(b, h, n, d, dt, splits)),

@@ -70,11 +70,12 @@ typedef struct {
     int32_t block_q;        /* Br: query rows per workgroup                            */
     int32_t block_k;        /* Bc: keys per K/V tile streamed through LDS              */
     int32_t waves;          /* wavefronts (64 lanes) per workgroup                     */
-    int32_t rows_per_wave;  /* query rows owned by each wave                           */
+    int32_t rows_per_wave;  /* query rows each wave computes                           */
     int32_t lds_bytes;      /* LDS per workgroup (K and V tiles, double-buffered)      */
     int64_t grid;           /* workgroups launched = B*H*ceil(N/Br) (*splits)          */
     int32_t kv_splits;      /* >1: key range split across workgroups, then merged      */
-    int32_t reserved;
+    int32_t wave_kv_splits; /* >1: a workgroup's waves share its query rows and split  */
+                            /*     the key tiles among themselves, merged in LDS       */
 } fa_plan;
 
 /*

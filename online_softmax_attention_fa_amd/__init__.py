@@ -40,11 +40,11 @@ class Plan(ctypes.Structure):
     _fields_ = [
         ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("waves", ctypes.c_int32),
         ("rows_per_wave", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("grid", ctypes.c_int64),
-        ("kv_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("kv_splits", ctypes.c_int32), ("wave_kv_splits", ctypes.c_int32),
     ]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 _lib = None

@@ -392,19 +392,24 @@ static hipError_t launch_splitkv_t(const FwdArgs& a, int64_t rows, hipStream_t s
 
 // ------------------------------------------------------------- fp32 kernel ---
 //
-// Same transposed formulation with v_mfma_f32_32x32x2_f32: each MFMA contracts two
-// dims (lane half h supplies dim 2s+h) or two keys.  Used for fp32 inputs, which are
-// small here; single LDS stage, 32 keys per tile, 32 queries per wave.
+// Same transposed formulation with v_mfma_f32_32x32x2_f32: each MFMA contracts two dims
+// (lane half h supplies dim 2s+h) or two keys.  fp32 inputs are small problems here, so
+// the kernel is built for latency: a workgroup owns 32 query rows, and its four waves
+// split the key tiles among themselves (tile j goes to wave j % 4), each keeping its own
+// running m, l and O for the 32 rows and its own K/V tile in LDS.  The four partial
+// states are then merged through LDS with the two-block rule of "FlashAttention
+// 硬件感知计算剖析" (section 二): M = max_w m_w, l = sum_w 2^(m_w - M) l_w,
+// O = sum_w 2^(m_w - M) O_w / l.  Four times fewer tiles run back to back per wave.
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
     constexpr int NT = 256, WAVES = 4, QPW = 32, BC = 32;
-    constexpr int BR = WAVES * QPW;
     constexpr int DB = D / 32;
     constexpr int DS = D / 2;
     constexpr int LD = D + 1;        // padded row stride (floats)
-    __shared__ float ks_[BC * LD];
-    __shared__ float vs_[BC * LD];
+    constexpr int WTILE = 2 * BC * LD;   // one wave's K and V tile (floats)
+    static_assert(WAVES * WTILE >= WAVES * QPW * D + 2 * WAVES * QPW, "merge area fits the tiles");
+    __shared__ float lds[WAVES * WTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -422,16 +427,18 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
     float* __restrict__ Oh = reinterpret_cast<float*>(a.o) + head;
     float* __restrict__ Lh = a.lse + (int64_t)bh * N;
 
-    const int q_wave = qblk * BR + wave * QPW;
-    const int query = q_wave + l32;
+    const int q0 = qblk * QPW;       // the workgroup's (and every wave's) first query row
+    const int query = q0 + l32;
     const float c = a.c;
+    float* ks_ = lds + wave * WTILE;
+    float* vs_ = ks_ + BC * LD;
 
     float qf[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = (query < N) ? Qh[(int64_t)query * D + 2 * s + h] : 0.f;
 
     int n_tiles = (N + BC - 1) / BC;
-    if (CAUSAL) n_tiles = min(n_tiles, (min(N, (qblk + 1) * BR) + BC - 1) / BC);
+    if (CAUSAL) n_tiles = min(n_tiles, (min(N, q0 + QPW) + BC - 1) / BC);
 
     f32x16 o[DB];
 #pragma unroll
@@ -440,17 +447,40 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
         for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
     float m = -INFINITY, lsum = 0.f;
 
-    for (int j = 0; j < n_tiles; ++j) {
-        const int kbase = j * BC;
-        __syncthreads();
-        for (int idx = tid; idx < BC * D; idx += NT) {
-            const int r = idx / D, col = idx % D;
-            const bool ok = kbase + r < N;
-            ks_[r * LD + col] = ok ? Kh[(int64_t)(kbase + r) * D + col] : 0.f;
-            vs_[r * LD + col] = ok ? Vh[(int64_t)(kbase + r) * D + col] : 0.f;
+    // A wave's next tile is fetched into registers (16 bytes per load) while it computes
+    // the current one.  Lane L holds float4 number L + 64 i of the tile (row-major).
+    constexpr int V4 = BC * D / 4 / 64;   // float4s per lane, K or V
+    f32x4 kreg[V4], vreg[V4];
+    auto fetch = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            const int idx = lane + 64 * i, r = idx / (D / 4), c4 = idx % (D / 4);
+            const bool ok = j * BC + r < N;
+            const int64_t off = (int64_t)(ok ? j * BC + r : 0) * D + 4 * c4;
+            kreg[i] = *reinterpret_cast<const f32x4*>(Kh + off);
+            vreg[i] = *reinterpret_cast<const f32x4*>(Vh + off);
+            if (!ok) kreg[i] = vreg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        __syncthreads();
-        if (CAUSAL && kbase > q_wave + QPW - 1) continue;
+    };
+    if (wave < n_tiles) fetch(wave);
+
+    for (int j = wave; j < n_tiles; j += WAVES) {
+        const int kbase = j * BC;
+        // this wave's tile into its LDS slot; LDS operations of one wave complete in
+        // order, so the reads of the previous tile are done before these writes land
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            const int idx = lane + 64 * i, r = idx / (D / 4), c4 = idx % (D / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ks_[r * LD + 4 * c4 + e] = kreg[i][e];
+                vs_[r * LD + 4 * c4 + e] = vreg[i][e];
+            }
+        }
+        if (j + WAVES < n_tiles) fetch(j + WAVES);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         f32x16 s;
 #pragma unroll
@@ -497,15 +527,39 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
         }
     }
 
+    // ---- merge the waves' partial states (a wave without tiles has m = -inf, l = 0, O = 0)
     const float lt = pair_sum(lsum);
-    const float inv = 1.0f / lt;
-    if (query < N) {
-        float* orow = Oh + (int64_t)query * D;
+    __syncthreads();                                  // every wave is done with its tiles
+    float* mo = lds;                                  // [WAVES][QPW][D] partial O
+    float* mm = lds + WAVES * QPW * D;                // [WAVES][QPW] m
+    float* ml = mm + WAVES * QPW;                     // [WAVES][QPW] l
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int t = 0; t < 16; ++t) orow[db * 32 + 8 * (t >> 2) + 4 * h + (t & 3)] = o[db][t] * inv;
-        if (h == 0) Lh[query] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+        for (int t = 0; t < 16; ++t)
+            mo[(wave * QPW + l32) * D + db * 32 + 8 * (t >> 2) + 4 * h + (t & 3)] = o[db][t];
+    if (h == 0) {
+        mm[wave * QPW + l32] = m;
+        ml[wave * QPW + l32] = lt;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < QPW * D; idx += NT) {
+        const int r = idx / D, col = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mm[w * QPW + r]);
+        float l = 0.f, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float mw = mm[w * QPW + r];
+            const float sc = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            l += sc * ml[w * QPW + r];
+            acc += sc * mo[(w * QPW + r) * D + col];
+        }
+        if (q0 + r < N) {
+            Oh[(int64_t)(q0 + r) * D + col] = acc / l;
+            if (col == 0) Lh[q0 + r] = (M + __builtin_amdgcn_logf(l)) * kLn2;
+        }
     }
 }
 

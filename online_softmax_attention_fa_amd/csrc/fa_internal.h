@@ -78,8 +78,8 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int fwd_lds_bytes(int dtype, int d, int block_k) {
     const int elt = dtype == FA_F32 ? 4 : 2;
     if (dtype == FA_F32) {
-        // K and V tiles padded by one element per row, single stage
-        return 2 * block_k * (d + 1) * elt;
+        // one K and one V tile per wave (4 waves), rows padded by one element
+        return 4 * 2 * block_k * (d + 1) * elt;
     }
     return 2 * (2 * block_k * d * elt);
 }
@@ -94,21 +94,24 @@ inline int fwd_lds_bytes(int dtype, int d, int block_k) {
 //  * Otherwise (N < 2048, or a grid that would leave most of its last round of
 //    workgroups idle, as B*H = 16, N = 4097 does): 4 waves per workgroup (Br = 128, two
 //    workgroups per CU), Bc = 64 at d = 128 and 128 at d = 64 (64 KiB of stages).
-// fp32: 4 waves x 32 rows, Bc = 32, single-stage LDS (latency-bound sizes only).
+// fp32: 32 query rows per workgroup, its 4 waves splitting the 32-key tiles among
+// themselves (latency-bound sizes only).
 inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal) {
     fa_plan p{};
     p.waves = 4;
     p.kv_splits = 1;
+    p.wave_kv_splits = 1;
     p.rows_per_wave = 32;
     if (dtype == FA_F32) {
         p.block_k = 32;
+        p.wave_kv_splits = 4;
     } else {
         const int64_t g8 = B * H * ceil_div(N, 8 * 32);   // workgroups at Br = 256
         const bool eight = N >= 2048 && (g8 >= 2 * kCus || g8 % kCus == 0);
         p.waves = eight ? 8 : 4;
         p.block_k = eight ? 128 : (d == 128 ? 64 : 128);
     }
-    p.block_q = p.waves * p.rows_per_wave;
+    p.block_q = p.waves * p.rows_per_wave / p.wave_kv_splits;
     p.lds_bytes = fwd_lds_bytes(dtype, (int)d, p.block_k);
     p.grid = B * H * ceil_div(N, p.block_q);
     (void)causal;

@@ -159,7 +159,7 @@ def test_plan_respects_lds_and_covers_rows(lib, dtype, d):
         p = fa.fa_fwd_plan(B, H, N, d, dtype)
         assert p["lds_bytes"] <= 160 * 1024
         assert p["waves"] * 64 <= 1024
-        assert p["block_q"] == p["waves"] * p["rows_per_wave"]
+        assert p["block_q"] * p["wave_kv_splits"] == p["waves"] * p["rows_per_wave"]
         assert p["rows_per_wave"] % 32 == 0 and p["block_k"] % 32 == 0
         assert p["grid"] == B * H * -(-N // p["block_q"])
         assert p["kv_splits"] >= 1

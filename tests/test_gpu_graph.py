@@ -1,0 +1,60 @@
+"""The entry points inside a captured HIP graph.
+
+"从零理解Flash Attention中的online softmax" (section 6.2) captures the whole attention
+computation in a graph so that replays skip the launch overhead.  The library's calls
+queue kernels on the caller's stream and allocate nothing, so they can be captured: here
+the forward, the split-KV forward (partial kernel + merge) and the backward (three
+kernels) go into one graph, which is replayed several times with eager work and
+synchronisations between replays; every replay must reproduce the eager results bit for
+bit.
+"""
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def test_forward_splitkv_backward_in_one_graph(gpu_lib):
+    import torch
+
+    fa = gpu_lib
+    B, H, N, d = 2, 3, 700, 128
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    q, k, v, do = (torch.randn(B, H, N, d, device="cuda", dtype=torch.bfloat16, generator=gen) for _ in range(4))
+    o, o2 = torch.empty_like(q), torch.empty_like(q)
+    lse, lse2 = (torch.empty(B, H, N, device="cuda", dtype=torch.float32) for _ in range(2))
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    splits = 3
+    ws_fwd = torch.empty(fa.fa_fwd_splitkv_workspace_bytes(B, H, N, d, torch.bfloat16, splits),
+                         dtype=torch.uint8, device="cuda")
+    ws_bwd = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d, torch.bfloat16), dtype=torch.uint8, device="cuda")
+
+    def work(stream):
+        fa.fa_fwd(q, k, v, o, lse, stream=stream)
+        fa.fa_fwd_splitkv(q, k, v, o2, lse2, splits=splits, workspace=ws_fwd, stream=stream)
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws_bwd, stream=stream)
+
+    # eager reference
+    work(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o, lse, o2, lse2, dq, dk, dv)]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):       # warm-up on the capture stream
+        work(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work(torch.cuda.current_stream())
+
+    outs = (o, lse, o2, lse2, dq, dk, dv)
+    for rep in range(4):
+        for t in outs:                # eager work between replays; outputs must be rewritten
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(("o", "lse", "o_split", "lse_split", "dq", "dk", "dv"), outs, ref):
+            assert torch.equal(t.view(torch.int8), r.view(torch.int8)), f"replay {rep}: {name} differs"
