@@ -15,6 +15,7 @@ namespace {
 
 constexpr int kVersion = 300;  // 0.3.0
 constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxGrid = int64_t(1) << 31;   // workgroups per launch (32-bit ids)
 
 struct DeviceInfo {
     std::once_flag once;
@@ -67,10 +68,11 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
         return FA_ERR_ALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+    const fa_plan plan = fa::choose_fwd_plan(B, H, N, d, dtype, causal);
+    if (plan.grid >= kMaxGrid) return FA_ERR_SHAPE;
     st = check_device();
     if (st != FA_OK) return st;
 
-    const fa_plan plan = fa::choose_fwd_plan(B, H, N, d, dtype, causal);
     fa::FwdArgs a;
     a.q = Q;
     a.k = K;
@@ -123,6 +125,7 @@ fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, f
     splits = effective_splits(B, H, N, Nk, d, splits);
     const int64_t tiles = fa::ceil_div(Nk, fa::splitkv_block_k(d));
     if (splits <= 1) return fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, dtype, stream, 0, Nk);
+    if (B * H * fa::ceil_div(N, 128) * splits >= kMaxGrid) return FA_ERR_SHAPE;
     const size_t need = fa::splitkv_workspace_bytes(B, H, N, d, splits);
     if (!ws || !aligned(ws, 256) || ws_bytes < need) return FA_ERR_WORKSPACE;
     st = check_device();
@@ -241,6 +244,8 @@ fa_status fa_quantize_fp8(const void* X, void* X8, float* scales, int64_t B, int
     if (st != FA_OK) return st;
     if (transpose != 0 && transpose != 1) return FA_ERR_UNSUPPORTED;
     if (B * H * N == 0) return FA_OK;
+    const int64_t per_head = transpose ? fa::fp8_padded_len(N) / fa::kFp8Block : fa::fp8_scale_blocks(N);
+    if (B * H * per_head >= kMaxGrid) return FA_ERR_SHAPE;
     if (!X || !X8 || !scales) return FA_ERR_NULL;
     if (!aligned(X, 16) || !aligned(X8, 16) || !aligned(scales, 4)) return FA_ERR_ALIGN;
     st = check_device();
@@ -328,7 +333,7 @@ fa_status fa_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype
     memset(plan, 0, sizeof(*plan));
     if (B * H * N == 0) return FA_OK;
     *plan = fa::choose_fwd_plan(B, H, N, d, dtype, causal);
-    return FA_OK;
+    return plan->grid >= kMaxGrid ? FA_ERR_SHAPE : FA_OK;
 }
 
 const char* fa_status_str(fa_status s) {

@@ -320,3 +320,14 @@ def test_splitkv_qk_without_gpu_stops_at_device_check(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible; the device check passes")
     assert _skv_qk(lib, splits=8) == 6
+
+
+def test_grids_beyond_32_bits_are_shape_errors(lib):
+    # B*H*ceil(N/128) fits the index math, but a launch would need 2^31 workgroups or more
+    B, H, N = 1 << 16, 1 << 8, 8192
+    assert lib.fa_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, B, H, N, 64, 0.125, fa.FA_F32, None) == 2   # 32-row blocks
+    plan = fa.Plan()
+    assert lib.fa_fwd_plan(B, H, N, 64, fa.FA_F32, 0, ctypes.byref(plan)) == 2
+    assert _skv(lib, B=B, H=H, N=N, d=64, splits=2) == 2
+    assert _q8(lib, B=B, H=H, N=N, d=64) == 2
+    assert _q8(lib, B=B, H=H, N=N, d=64, transpose=1) == 2
