@@ -57,6 +57,7 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
     FA_ERR_SHAPE = 2,       /* B, H or N negative, or sizes overflow the index math */
+                            /* or a launch's 2^31 workgroup ids                       */
     FA_ERR_UNSUPPORTED = 3, /* head dim not in {64, 128}, or unknown dtype           */
     FA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte (LSE: 4-byte) aligned */
     FA_ERR_SCALE = 5,       /* scale is not finite or not > 0                        */
@@ -71,7 +72,7 @@ typedef struct {
     int32_t block_k;        /* Bc: keys per K/V tile streamed through LDS              */
     int32_t waves;          /* wavefronts (64 lanes) per workgroup                     */
     int32_t rows_per_wave;  /* query rows each wave computes                           */
-    int32_t lds_bytes;      /* LDS per workgroup (K and V tiles, double-buffered)      */
+    int32_t lds_bytes;      /* LDS per workgroup (its K and V tile buffers)            */
     int64_t grid;           /* workgroups launched = B*H*ceil(N/Br) (*splits)          */
     int32_t kv_splits;      /* >1: key range split across workgroups, then merged      */
     int32_t wave_kv_splits; /* >1: a workgroup's waves share its query rows and split  */
