@@ -188,3 +188,42 @@ def wl_dtype_code(dtype):
     import online_softmax_attention_fa_amd as fa
 
     return {"fp32": fa.FA_F32, "fp16": fa.FA_F16, "bf16": fa.FA_BF16}[dtype]
+
+
+# ------------------------------------------------------------ non-finite inputs ---
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_non_finite_inputs_propagate(gpu_lib, dtype):
+    """A NaN or Inf in query row i reaches row i's output and LSE only; a NaN in key row j
+    reaches every row (each score row contains key j); a NaN in value row j reaches every
+    output row but no LSE.  Rows not touched stay equal to the oracle."""
+    import torch
+
+    N, d = 300, 64
+    q, k, v = _random_qkv(1, 1, N, d, dtype, seed=7)
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(d))
+    cases = {
+        "q row NaN": (q.copy(), k, v, "q"),
+        "q row Inf": (q.copy(), k, v, "qinf"),
+        "k row NaN": (q, k.copy(), v, "k"),
+        "v row NaN": (q, k, v.copy(), "v"),
+    }
+    cases["q row NaN"][0][0, 0, 77, 5] = np.nan
+    cases["q row Inf"][0][0, 0, 140, 3] = np.inf
+    cases["k row NaN"][1][0, 0, 200, 9] = np.nan
+    cases["v row NaN"][2][0, 0, 31, 2] = np.nan
+    for name, (qq, kk, vv, kind) in cases.items():
+        O, L = run_fwd(gpu_lib, qq, kk, vv, dtype)
+        bad_o = ~np.isfinite(O[0, 0])
+        bad_l = ~np.isfinite(L[0, 0])
+        if kind in ("q", "qinf"):
+            row = 77 if kind == "q" else 140
+            assert bad_o[row].all() or bad_l[row], f"{name}: row {row} stayed finite"
+            others = np.arange(N) != row
+            assert not bad_o[others].any() and not bad_l[others].any(), f"{name}: leaked to other rows"
+            compare(O[:, :, others], L[:, :, others], O_ref[:, :, others], L_ref[:, :, others], dtype, name)
+        elif kind == "k":
+            assert bad_o.all(axis=1).all() and bad_l.all(), f"{name}: some row stayed finite"
+        else:
+            assert bad_o[:, 2].all(), f"{name}: the poisoned column stayed finite in some row"
+            assert not bad_l.any(), f"{name}: a NaN value leaked into the LSE"
