@@ -10,6 +10,7 @@
 
 #include "fa_fp8.h"
 #include "fa_internal.h"
+#include "fa_splitkv.h"
 
 namespace {
 

@@ -118,30 +118,6 @@ inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int d
     return p;
 }
 
-// Split-KV (key ranges processed by separate workgroups, then merged by their LSE).
-constexpr int kMaxKvSplits = 64;
-// Key tile of the split-KV path (the 4-wave tile-loop kernel's Bc).
-inline int splitkv_block_k(int64_t d) { return d == 128 ? 64 : 128; }
-// Workspace of fa_fwd_splitkv: partial O (fp32) and partial LSE per split, 256-byte aligned.
-inline size_t splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int splits) {
-    if (splits <= 1) return 0;
-    const size_t rows = (size_t)(B * H * N);
-    const size_t o_bytes = (size_t)splits * rows * (size_t)d * sizeof(float);
-    const size_t l_bytes = (size_t)splits * rows * sizeof(float);
-    return (o_bytes + 255) / 256 * 256 + (l_bytes + 255) / 256 * 256;
-}
-// The chooser's split count: enough workgroups for two per CU, each split at least two
-// key tiles; 1 when the plain grid already fills the chip.
-inline int choose_kv_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
-    const int64_t grid = B * H * ceil_div(Nq, 128);
-    const int64_t tiles = ceil_div(Nk, splitkv_block_k(d));
-    if (grid >= 2 * kCus) return 1;
-    int64_t s = ceil_div(2 * kCus, grid);
-    if (s > tiles / 2) s = tiles / 2;
-    if (s > kMaxKvSplits) s = kMaxKvSplits;
-    return s < 2 ? 1 : (int)s;
-}
-
 }  // namespace fa
 
 // Launchers implemented in fa_fwd_kernel.hip.  Return 0 on success or the

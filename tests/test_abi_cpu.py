@@ -212,6 +212,12 @@ def test_splitkv_workspace_and_split_choice(lib):
     for N in (128, 256, 1000, 4097, 16384):
         s = lib.fa_fwd_splitkv_splits(1, 1, N, 128, fa.FA_BF16)
         assert 1 <= s <= 64 and (s == 1 or -(-N // 64) >= 2 * s)
+    # a full grid is split only when its last round of workgroups is nearly empty:
+    # B=2 H=8 N=4097 d=128 has 528 blocks of 128 rows on 512 slots
+    assert lib.fa_fwd_splitkv_splits(2, 8, 4097, 128, fa.FA_BF16) == 3
+    assert lib.fa_fwd_splitkv_splits(4, 16, 2048, 64, fa.FA_BF16) == 1      # two full rounds
+    assert lib.fa_fwd_splitkv_splits(2, 16, 8192, 128, fa.FA_BF16) == 1     # 1024 blocks
+    assert lib.fa_fwd_splitkv_splits(8, 32, 4097, 128, fa.FA_BF16) == 1     # many rounds
 
 
 def test_splitkv_validation(lib):
