@@ -9,9 +9,9 @@ namespace fa {
 // ------------------------------------------------------------ block-scaled fp8 ---
 // Q, K and V in OCP E4M3 with one power-of-two scale per 64 rows of a (batch, head).
 constexpr int kFp8Block = 64;      // rows per scale block
-constexpr int kFp8Bc = 128;        // keys per LDS tile of the fp8 forward
-// V^T rows are padded to a whole number of key tiles (padding holds code 0).
-inline int64_t fp8_padded_len(int64_t N) { return ceil_div(N, kFp8Bc) * kFp8Bc; }
+constexpr int kFp8TileK = 64;      // keys per LDS tile of the fp8 forward (one scale block)
+constexpr int kFp8Pad = 128;       // V^T rows are padded to a multiple of this (code 0)
+inline int64_t fp8_padded_len(int64_t N) { return ceil_div(N, kFp8Pad) * kFp8Pad; }
 inline int64_t fp8_scale_blocks(int64_t N) { return ceil_div(N, kFp8Block); }
 
 // Quantiser arguments.  One workgroup per (batch*head, 64-row block).
