@@ -58,7 +58,7 @@ namespace fa {
 // V[k0 + e][d0 + c] for e = 0..3: four keys of its own column.
 
 template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool SPLIT = false>
-__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource types exist only in the device pass
     constexpr int NT = 64 * WAVES, QPW = 32, BR = WAVES * QPW;
     constexpr int KB = BC / 32;       // 32-key row blocks of S^T per tile
@@ -584,6 +584,7 @@ static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int cau
     if (d == 64 && p.block_k == 128 && p.waves == 8) return launch_t<T, 64, 128, 8>(a, causal, st);
     if (d == 128 && p.block_k == 64 && p.waves == 4) return launch_t<T, 128, 64, 4>(a, causal, st);
     if (d == 64 && p.block_k == 128 && p.waves == 4) return launch_t<T, 64, 128, 4>(a, causal, st);
+    if (d == 128 && p.block_k == 32 && p.waves == 4) return launch_t<T, 128, 32, 4>(a, causal, st);
     return hipErrorInvalidConfiguration;
 }
 

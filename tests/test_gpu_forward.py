@@ -159,15 +159,19 @@ def test_empty_problem_is_a_no_op(gpu_lib):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N,causal", [(2049, False), (3000, False), (8191, False), (2500, True)])
+@pytest.mark.parametrize("N,causal", [(2049, False), (3000, False), (8191, False), (2500, True), (4099, True)])
 def test_eight_wave_plan_sampled(gpu_lib, dtype, d, N, causal):
-    # B*H = 64 puts these on the 8-wave, 128-key-tile plan; rows past the last full query
-    # block and keys past the last full tile exercise the masks.
+    # B*H = 64 puts these on the 8-wave, 128-key-tile plan (causal at d = 128: the 4-wave,
+    # 32-key-tile plan at three waves per SIMD); rows past the last full query block and keys
+    # past the last full tile exercise the masks.
     import torch
 
     B, H = 4, 16
     plan = gpu_lib.fa_fwd_plan(B, H, N, d, wl_dtype_code(dtype), causal=causal)
-    assert plan["waves"] == 8 and plan["block_k"] == 128
+    if causal and d == 128:
+        assert plan["waves"] == 4 and plan["block_k"] == 32
+    else:
+        assert plan["waves"] == 8 and plan["block_k"] == 128
     q, k, v = _random_qkv(B, H, N, d, dtype, seed=N * 7 + d + int(causal))
     tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
     o, lse = gpu_lib.fa_fwd(tq, tk, tv, causal=causal)
