@@ -48,8 +48,8 @@ fa_status check_problem(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
     if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
     if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    // per-head element offsets are 32-bit inside the kernels; grid is 32-bit
-    if (N > 0 && N * d >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+    // per-head byte offsets (16-bit elements) are 32-bit signed inside the kernels
+    if (N > 0 && N * d >= (int64_t(1) << 30)) return FA_ERR_SHAPE;
     if (B > 0 && H > (int64_t(1) << 31) / B) return FA_ERR_SHAPE;
     const int64_t bh = B * H;
     if (bh > 0 && N > 0 && bh * fa::ceil_div(N, 128) >= (int64_t(1) << 31)) return FA_ERR_SHAPE;

@@ -337,3 +337,9 @@ def test_grids_beyond_32_bits_are_shape_errors(lib):
     assert _skv(lib, B=B, H=H, N=N, d=64, splits=2) == 2
     assert _q8(lib, B=B, H=H, N=N, d=64) == 2
     assert _q8(lib, B=B, H=H, N=N, d=64, transpose=1) == 2
+
+
+def test_heads_beyond_32_bit_byte_offsets_are_shape_errors(lib):
+    # one head of 2^23 rows x 128 dims is 2 GiB of bf16: past the kernels' 32-bit offsets
+    assert lib.fa_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1 << 23, 128, 0.125, fa.FA_BF16, None) == 2
+    assert lib.fa_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, (1 << 23) - 1, 128, 0.125, fa.FA_BF16, None) in (0, 6)
