@@ -197,3 +197,19 @@ def test_backward_large_workload_sampled(gpu_lib):
         compare_grad(to_host(dk[b, h].index_select(0, cc)), dk_ref, w.dtype, f"b{b} h{h} dK", mass=m_dk)
         compare_grad(to_host(dv[b, h].index_select(0, cc)), dv_ref, w.dtype, f"b{b} h{h} dV", mass=m_dv)
     print(f"{w.name}: dQ worst {worst}; dK/dV heads {heads}")
+
+
+_rng = np.random.default_rng(20261203)
+RANDOM_CASES = [dict(B=int(_rng.integers(1, 3)), H=int(_rng.integers(1, 4)), N=int(_rng.integers(2, 520)),
+                     d=int(_rng.choice([64, 128])), dtype=str(_rng.choice(["bf16", "fp16"])),
+                     causal=bool(_rng.integers(0, 2)), seed=i) for i in range(10)]
+
+
+@pytest.mark.parametrize("c", RANDOM_CASES,
+                         ids=lambda c: "B{B}H{H}N{N}d{d}-{dtype}-{}".format("causal" if c["causal"] else "full", **c))
+def test_backward_random_shapes(gpu_lib, c):
+    """Seeded random shapes, causal or not, through the library's forward and backward."""
+    q, k, v, do = _inputs(c["B"], c["H"], c["N"], c["d"], c["dtype"], seed=7000 + c["seed"])
+    got = _gpu_grads(gpu_lib, q, k, v, do, c["dtype"], causal=c["causal"])
+    ref = _oracle_grads(q, k, v, do, scale_of(c["d"]), c["dtype"], causal=c["causal"])
+    _check_all(got, ref, c["dtype"], str(c))
