@@ -25,8 +25,9 @@ ONE JSON line on stdout (everything else goes to stderr):
              cores, with the GPU output checked on the same rows
   sweep      (--sweep only) forward time of the smaller workloads (fp32 B1 H1 N256 d64,
              bf16 B4 H16 N2048 d64, fp16 B1 H32 N16384 d128, bf16 B2 H8 N4097 d128), the
-             causal and split-KV variants, and short sequences at B*H=1024 d=128 where
-             the kernel is bounded by HBM bandwidth; min and median of per-launch events
+             causal and split-KV variants, the fp8 forward causal at d=128 and at d=64,
+             short sequences at B*H=1024 d=128 where the kernel is bounded by HBM
+             bandwidth, and a decode shape; min and median of per-launch events
 """
 
 from __future__ import annotations
@@ -227,6 +228,8 @@ def sweep(fa, stream, steps=20):
         ("fp16 B1 H32 N16384 d128", 1, 32, 16384, 128, torch.float16, "plain"),
         ("bf16 B2 H8 N4097 d128", 2, 8, 4097, 128, torch.bfloat16, "plain"),
         ("bf16 B4 H32 N16384 d128 causal", 4, 32, 16384, 128, torch.bfloat16, "causal"),
+        ("fp8 B4 H32 N16384 d128 causal", 4, 32, 16384, 128, torch.bfloat16, "fp8causal"),
+        ("fp8 B4 H32 N16384 d64", 4, 32, 16384, 64, torch.bfloat16, "fp8"),
         ("bf16 B1 H1 N16384 d128", 1, 1, 16384, 128, torch.bfloat16, "plain"),
         ("bf16 B1 H1 N16384 d128 split-KV", 1, 1, 16384, 128, torch.bfloat16, "split"),
         ("bf16 B1 H8 N4096 d128", 1, 8, 4096, 128, torch.bfloat16, "plain"),
@@ -259,6 +262,12 @@ def sweep(fa, stream, steps=20):
             with torch.cuda.graph(graph):
                 fa.fa_fwd(q, k, v, o, lse, scale=sc)
             fn = graph.replay
+        elif mode in ("fp8", "fp8causal"):
+            # codes and scales resident (quantised once, outside the timed launches)
+            (q8, qs), (k8, ks), (vt8, vs) = (fa.fa_quantize_fp8(q), fa.fa_quantize_fp8(k),
+                                             fa.fa_quantize_fp8(v, transpose=True))
+            fn = lambda: fa.fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, o, lse, scale=sc, stream=stream,
+                                       causal=(mode == "fp8causal"))
         elif mode == "split":
             splits = fa.fa_fwd_splitkv_splits(b, h, n, d, dt)
             ws = torch.empty(max(1, fa.fa_fwd_splitkv_workspace_bytes(b, h, n, d, dt, splits)),
@@ -268,9 +277,10 @@ def sweep(fa, stream, steps=20):
             fn = lambda: fa.fa_fwd(q, k, v, o, lse, scale=sc, stream=stream, causal=(mode == "causal"))
         t = launch_times(fn, stream, steps)
         tmin, tmed = min(t), statistics.median(t)
-        flops = 4.0 * b * h * nq * n * d * (0.5 if mode == "causal" else 1.0)
-        nbytes = (2.0 * nq + 2.0 * n) * b * h * d * q.element_size() + 4.0 * b * h * nq
-        peak = 157.3 if dt == torch.float32 else PEAK_BF16_TFLOPS
+        flops = 4.0 * b * h * nq * n * d * (0.5 if mode in ("causal", "fp8causal") else 1.0)
+        in_bytes = 1 if mode.startswith("fp8") else q.element_size()
+        nbytes = (nq + 2.0 * n) * b * h * d * in_bytes + nq * b * h * d * q.element_size() + 4.0 * b * h * nq
+        peak = 157.3 if dt == torch.float32 else PEAK_FP8_TFLOPS if mode.startswith("fp8") else PEAK_BF16_TFLOPS
         r = {"case": name, "min_ms": round(tmin, 4), "median_ms": round(tmed, 4),
              "tflops": round(flops / (tmed * 1e-3) / 1e12, 2),
              "pct_of_mfma_peak": round(100 * flops / (tmed * 1e-3) / 1e12 / peak, 2),
@@ -280,7 +290,7 @@ def sweep(fa, stream, steps=20):
         rows.append(r)
         log(f"sweep {name}: median {tmed * 1e3:.1f} us, min {tmin * 1e3:.1f} us, {r['tflops']} TFLOP/s "
             f"({r['pct_of_mfma_peak']}% of MFMA peak), {r['gbps']} GB/s algorithmic")
-        del q, k, v, o, lse
+        del q, k, v, o, lse, fn
     return rows
 
 

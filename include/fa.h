@@ -217,6 +217,13 @@ fa_status fa_quantize_fp8(const void* X, void* X8, float* scales, int64_t B, int
 fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale,
                      const float* k_scale, const float* v_scale, void* O, float* LSE, int64_t B,
                      int64_t H, int64_t N, int64_t d, float scale, fa_dtype out_dtype, void* stream);
+/*
+ * fa_fwd_fp8 with the causal mask of fa_fwd_causal: query row i attends to keys 0..i.
+ * Same arguments, layouts and errors.
+ */
+fa_status fa_fwd_fp8_causal(const void* Q8, const void* K8, const void* Vt8, const float* q_scale,
+                            const float* k_scale, const float* v_scale, void* O, float* LSE, int64_t B,
+                            int64_t H, int64_t N, int64_t d, float scale, fa_dtype out_dtype, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(fa_status s);

@@ -27,7 +27,7 @@ STATUS = {
 EXPORTS = ("fa_fwd", "fa_fwd_causal", "fa_fwd_plan", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_splits",
            "fa_fwd_splitkv", "fa_fwd_splitkv_qk_workspace_bytes", "fa_fwd_splitkv_qk_splits", "fa_fwd_splitkv_qk",
            "fa_fp8_padded_len", "fa_fp8_scale_blocks", "fa_quantize_fp8", "fa_fwd_fp8",
-           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal", "fa_status_str", "fa_version")
+           "fa_fwd_fp8_causal",           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal", "fa_status_str", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -85,8 +85,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fp8_scale_blocks.restype = I64
     lib.fa_quantize_fp8.argtypes = [P, P, P, I64, I64, I64, I64, I, ctypes.c_int32, P]
     lib.fa_quantize_fp8.restype = I
-    lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, P]
-    lib.fa_fwd_fp8.restype = I
+    for name in ("fa_fwd_fp8", "fa_fwd_fp8_causal"):
+        getattr(lib, name).argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, P]
+        getattr(lib, name).restype = I
     lib.fa_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     bwd_args = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, I64, I64, I64, I64, F, I, P]
@@ -270,14 +271,17 @@ def fa_quantize_fp8(x, transpose=False, x8=None, scales=None, stream=None):
     return x8, scales
 
 
-def fa_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, o=None, lse=None, scale=None, out_dtype=None, stream=None):
-    """O, LSE of attention on block-scaled E4M3 inputs through ``fa_fwd_fp8``.
+def fa_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, o=None, lse=None, scale=None, out_dtype=None, stream=None,
+               causal=False):
+    """O, LSE of attention on block-scaled E4M3 inputs through ``fa_fwd_fp8`` (or
+    ``fa_fwd_fp8_causal`` when ``causal``).
 
     q8, k8: uint8 [B, H, N, d]; vt8: uint8 [B, H, d, Np]; scales fp32 [B, H, nb].
     O has ``out_dtype`` (default bfloat16).  Returns (o, lse)."""
     import torch
 
     lib = load()
+    name = "fa_fwd_fp8_causal" if causal else "fa_fwd_fp8"
     B, H, N, d = q8.shape
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     nb = fa_fp8_scale_blocks(N)
@@ -293,11 +297,15 @@ def fa_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, o=None, lse=None, scale=N
         scale = 1.0 / math.sqrt(d)
     o = torch.empty((B, H, N, d), dtype=out_dtype, device=q8.device) if o is None else o
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    if tuple(o.shape) != (B, H, N, d) or o.dtype != out_dtype or not o.is_contiguous():
+        raise ValueError("o must be contiguous [B, H, N, d] of out_dtype")
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, N]")
     with torch.cuda.device(q8.device):
-        st = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
-                            v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
-                            dtype_code(out_dtype), _stream_handle(stream))
-    _check(st, "fa_fwd_fp8")
+        st = getattr(lib, name)(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_scale.data_ptr(),
+                                k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                                float(scale), dtype_code(out_dtype), _stream_handle(stream))
+    _check(st, name)
     return o, lse
 
 

@@ -263,9 +263,10 @@ fa_status fa_quantize_fp8(const void* X, void* X8, float* scales, int64_t B, int
     return e == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 
-fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale, const float* k_scale,
-                     const float* v_scale, void* O, float* LSE, int64_t B, int64_t H, int64_t N, int64_t d,
-                     float scale, fa_dtype out_dtype, void* stream) {
+namespace {
+fa_status fwd_fp8_common(const void* Q8, const void* K8, const void* Vt8, const float* q_scale, const float* k_scale,
+                         const float* v_scale, void* O, float* LSE, int64_t B, int64_t H, int64_t N, int64_t d,
+                         float scale, fa_dtype out_dtype, void* stream, int causal) {
     fa_status st = check_fp8_problem(B, H, N, d, out_dtype);
     if (st != FA_OK) return st;
     if (B * H * N == 0) return FA_OK;
@@ -291,8 +292,21 @@ fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const floa
     a.n_qblk = (int)fa::ceil_div(N, fa::kFp8BlockQ);
     a.n_blocks = (int)(B * H * a.n_qblk);
     a.c = (float)((double)scale * 1.4426950408889634074);
-    const int e = fa_launch_fwd_fp8(a, out_dtype, (int)d, stream);
+    const int e = fa_launch_fwd_fp8(a, out_dtype, (int)d, causal, stream);
     return e == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+}  // namespace
+
+fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale, const float* k_scale,
+                     const float* v_scale, void* O, float* LSE, int64_t B, int64_t H, int64_t N, int64_t d,
+                     float scale, fa_dtype out_dtype, void* stream) {
+    return fwd_fp8_common(Q8, K8, Vt8, q_scale, k_scale, v_scale, O, LSE, B, H, N, d, scale, out_dtype, stream, 0);
+}
+
+fa_status fa_fwd_fp8_causal(const void* Q8, const void* K8, const void* Vt8, const float* q_scale,
+                            const float* k_scale, const float* v_scale, void* O, float* LSE, int64_t B, int64_t H,
+                            int64_t N, int64_t d, float scale, fa_dtype out_dtype, void* stream) {
+    return fwd_fp8_common(Q8, K8, Vt8, q_scale, k_scale, v_scale, O, LSE, B, H, N, d, scale, out_dtype, stream, 1);
 }
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype) {

@@ -173,7 +173,7 @@ __device__ __forceinline__ int swz_fp8(int row) {
 // workgroup needs 32 KiB of LDS and the registers fit; the third wave hides more of each
 // wave's MFMA -> softmax -> MFMA dependency chain than the 128-key tile's longer steps did
 // (8% faster at B=4 H=32 N=16384 d=128).
-template <typename TO, int D, int WAVES>
+template <typename TO, int D, int WAVES, bool CAUSAL>
 __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int NT = 64 * WAVES, QPW = 32, BR = WAVES * QPW, BC = kFp8TileK;
@@ -202,7 +202,8 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
 
     const int bid = remap_xcd(blockIdx.x, a.n_blocks);
     const int bh = bid / a.n_qblk;
-    const int qblk = bid - bh * a.n_qblk;
+    int qblk = bid - bh * a.n_qblk;
+    if (CAUSAL) qblk = a.n_qblk - 1 - qblk;   // longest rows first
     const unsigned char* __restrict__ Qh = a.q8 + (int64_t)bh * N * D;
     const unsigned char* __restrict__ Kh = a.k8 + (int64_t)bh * N * D;
     const unsigned char* __restrict__ Vh = a.vt8 + (int64_t)bh * D * NP;
@@ -284,7 +285,8 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
     float m = -INFINITY, lsum = 0.f;
-    const int n_tiles = (N + BC - 1) / BC;
+    int n_tiles = (N + BC - 1) / BC;
+    if (CAUSAL) n_tiles = min(n_tiles, (min(N, (qblk + 1) * BR) + BC - 1) / BC);
 
     auto compute_tile = [&](int j, const lds_u8* sbase) {
         const int kbase = j * BC;
@@ -316,7 +318,16 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
         }
         __builtin_amdgcn_s_setprio(0);
 
-        if (kbase + BC > N) {   // keys past N
+        if (CAUSAL) {
+            if (kbase + BC > N || kbase + BC - 1 > q_wave) {   // keys after the query or past N
+                const int last = min(query, N - 1) - kbase - 4 * h;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int t = 0; t < 16; ++t)
+                        if (kb * 32 + 8 * (t >> 2) + (t & 3) > last) s[kb][t] = -INFINITY;
+            }
+        } else if (kbase + BC > N) {   // keys past N
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -399,6 +410,8 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
     for (int j = 0; j < n_tiles; j += 2) {
+        // (causal: every wave computes every tile up to the block's diagonal; skipping the
+        // few tiles past a wave's own rows costs more in registers than it saves)
         if (j + 1 < n_tiles) issue_tile(j + 1, stage1);
         compute_tile(j, stage0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -440,9 +453,12 @@ int launch_quant_t(const QuantArgs& a, int64_t bh, int transpose, void* stream) 
 }
 
 template <typename TO, int D>
-int launch_fp8_t(const Fp8Args& a, void* stream) {
+int launch_fp8_t(const Fp8Args& a, int causal, void* stream) {
     constexpr int WAVES = kFp8BlockQ / 32;
-    hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, WAVES>), dim3(a.n_blocks), dim3(64 * WAVES), 0, (hipStream_t)stream, a);
+    if (causal)
+        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, WAVES, true>), dim3(a.n_blocks), dim3(64 * WAVES), 0, (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, WAVES, false>), dim3(a.n_blocks), dim3(64 * WAVES), 0, (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 
@@ -456,8 +472,8 @@ int fa_launch_quantize_fp8(const fa::QuantArgs& a, int64_t bh, int in_dtype, int
                     : fa::launch_quant_t<_Float16, 64>(a, bh, transpose, stream);
 }
 
-int fa_launch_fwd_fp8(const fa::Fp8Args& a, int out_dtype, int d, void* stream) {
+int fa_launch_fwd_fp8(const fa::Fp8Args& a, int out_dtype, int d, int causal, void* stream) {
     if (out_dtype == FA_BF16)
-        return d == 128 ? fa::launch_fp8_t<__bf16, 128>(a, stream) : fa::launch_fp8_t<__bf16, 64>(a, stream);
-    return d == 128 ? fa::launch_fp8_t<_Float16, 128>(a, stream) : fa::launch_fp8_t<_Float16, 64>(a, stream);
+        return d == 128 ? fa::launch_fp8_t<__bf16, 128>(a, causal, stream) : fa::launch_fp8_t<__bf16, 64>(a, causal, stream);
+    return d == 128 ? fa::launch_fp8_t<_Float16, 128>(a, causal, stream) : fa::launch_fp8_t<_Float16, 64>(a, causal, stream);
 }

@@ -115,17 +115,18 @@ def dequantize_blocks(codes, scales, block=BLOCK_ROWS):
     return v * row_scale[..., None]
 
 
-def attention_fp8(Qc, Qs, Kc, Ks, Vc, Vs, scale, block=BLOCK_ROWS, return_p=False):
-    """Attention of the dequantised tensors, per head ([N, d] codes, [nb] scales)."""
+def attention_fp8(Qc, Qs, Kc, Ks, Vc, Vs, scale, block=BLOCK_ROWS, return_p=False, causal=False):
+    """Attention of the dequantised tensors, per head ([N, d] codes, [nb] scales); with
+    ``causal`` the mask of ``attention_forward`` (keys after the query row dropped)."""
     Q = dequantize_blocks(Qc, Qs, block)
     K = dequantize_blocks(Kc, Ks, block)
     V = dequantize_blocks(Vc, Vs, block)
-    return attention_forward(Q, K, V, scale, return_p=return_p)
+    return attention_forward(Q, K, V, scale, causal=causal, return_p=return_p)
 
 
-def attention_fp8_rows(Qc, Qs, Kc, Ks, Vc, Vs, scale, rows, block=BLOCK_ROWS):
+def attention_fp8_rows(Qc, Qs, Kc, Ks, Vc, Vs, scale, rows, block=BLOCK_ROWS, causal=False):
     """``attention_fp8`` for query rows ``rows`` of one head only."""
     Q = dequantize_blocks(Qc, Qs, block)
     K = dequantize_blocks(Kc, Ks, block)
     V = dequantize_blocks(Vc, Vs, block)
-    return attention_rows(Q, K, V, scale, rows)
+    return attention_rows(Q, K, V, scale, rows, causal=causal)

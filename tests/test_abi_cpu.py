@@ -7,6 +7,7 @@ device check with FA_ERR_DEVICE.
 """
 
 import ctypes
+import functools
 import os
 import re
 
@@ -248,8 +249,9 @@ def _q8(lib, x=FAKE, x8=FAKE, sc=FAKE, B=1, H=2, N=100, d=128, dtype=fa.FA_BF16,
 
 
 def _f8(lib, q=FAKE, k=FAKE, v=FAKE, qs=FAKE, ks=FAKE, vs=FAKE, o=FAKE, lse=FAKE, B=1, H=2, N=100, d=128,
-        scale=0.125, dtype=fa.FA_BF16):
-    return lib.fa_fwd_fp8(q, k, v, qs, ks, vs, o, lse, B, H, N, d, scale, dtype, None)
+        scale=0.125, dtype=fa.FA_BF16, causal=False):
+    fn = lib.fa_fwd_fp8_causal if causal else lib.fa_fwd_fp8
+    return fn(q, k, v, qs, ks, vs, o, lse, B, H, N, d, scale, dtype, None)
 
 
 def test_fp8_sizes(lib):
@@ -261,7 +263,9 @@ def test_fp8_sizes(lib):
     assert lib.fa_fp8_scale_blocks(0) == 0
 
 
-def test_fp8_validation_order_and_codes(lib):
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_validation_order_and_codes(lib, causal):
+    f8 = functools.partial(_f8, causal=causal)
     assert _q8(lib, N=-1) == 2
     assert _q8(lib, d=96) == 3
     assert _q8(lib, dtype=fa.FA_F32) == 3
@@ -270,16 +274,16 @@ def test_fp8_validation_order_and_codes(lib):
     assert _q8(lib, x8=None) == 1
     assert _q8(lib, sc=FAKE + 2) == 4
     assert _q8(lib, x8=FAKE + 8) == 4
-    assert _f8(lib, B=-1) == 2
-    assert _f8(lib, dtype=fa.FA_F32) == 3
-    assert _f8(lib, d=32) == 3
-    assert _f8(lib, q=None, N=0) == 0
-    assert _f8(lib, vs=None) == 1
-    assert _f8(lib, v=FAKE + 4) == 4
-    assert _f8(lib, ks=FAKE + 1) == 4
-    assert _f8(lib, scale=-1.0) == 5
+    assert f8(lib, B=-1) == 2
+    assert f8(lib, dtype=fa.FA_F32) == 3
+    assert f8(lib, d=32) == 3
+    assert f8(lib, q=None, N=0) == 0
+    assert f8(lib, vs=None) == 1
+    assert f8(lib, v=FAKE + 4) == 4
+    assert f8(lib, ks=FAKE + 1) == 4
+    assert f8(lib, scale=-1.0) == 5
     # the padded V^T head must fit 32-bit byte offsets
-    assert _f8(lib, N=(1 << 24) - 1, d=128) == 2
+    assert f8(lib, N=(1 << 24) - 1, d=128) == 2
 
 
 def test_fp8_valid_calls_without_gpu_stop_at_device_check(lib):
@@ -290,6 +294,7 @@ def test_fp8_valid_calls_without_gpu_stop_at_device_check(lib):
     assert _q8(lib) == 6
     assert _q8(lib, transpose=1) == 6
     assert _f8(lib) == 6
+    assert _f8(lib, causal=True) == 6
 
 
 def _skv_qk(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=WS, ws_bytes=1 << 40, B=2, H=4, Nq=1, Nk=5000,

@@ -76,10 +76,12 @@ def test_quantize_matches_oracle(gpu_lib, dtype, d, N):
 
 # ------------------------------------------------------------------ forward ---
 
-def _fp8_bound(Qd, Kd, Vd, vcodes, vscales, scale, rows):
+def _fp8_bound(Qd, Kd, Vd, vcodes, vscales, scale, rows, causal=False):
     """The elementwise O error bound and the per-row LSE bound of the module docstring,
-    for query rows ``rows``."""
+    for query rows ``rows`` (W and Z of the masked scores when ``causal``)."""
     S = scale * (Qd[rows] @ Kd.T)
+    if causal:
+        S = np.where(np.arange(Kd.shape[0])[None, :] <= np.asarray(rows)[:, None], S, -np.inf)
     E = np.exp(S - S.max(axis=1, keepdims=True))
     Z = E.sum(axis=1, keepdims=True)
     W = E / Z
@@ -90,27 +92,27 @@ def _fp8_bound(Qd, Kd, Vd, vcodes, vscales, scale, rows):
     return o_bound, dS[:, 0]
 
 
-def _run_fp8(fa, q, k, v, in_dtype, out_dtype, scale=None):
+def _run_fp8(fa, q, k, v, in_dtype, out_dtype, scale=None, causal=False):
     import torch
 
     tq, tk, tv = (to_device(x, in_dtype) for x in (q, k, v))
     q8, qs = fa.fa_quantize_fp8(tq)
     k8, ks = fa.fa_quantize_fp8(tk)
     vt8, vs = fa.fa_quantize_fp8(tv, transpose=True)
-    o, lse = fa.fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, scale=scale,
+    o, lse = fa.fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, scale=scale, causal=causal,
                            out_dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float16)
     torch.cuda.synchronize()
     return to_host(o), lse.cpu().numpy().astype(np.float64)
 
 
-def _check_head(O, L, q, k, v, scale, out_dtype, rows, what):
+def _check_head(O, L, q, k, v, scale, out_dtype, rows, what, causal=False):
     """Oracle for one head (on the requested rows) and the bound check."""
     qc, qs = ofp8.quantize_blocks(q)
     kc, ks = ofp8.quantize_blocks(k)
     vc, vs = ofp8.quantize_blocks(v)
-    O_ref, L_ref = ofp8.attention_fp8_rows(qc, qs, kc, ks, vc, vs, scale, rows)
+    O_ref, L_ref = ofp8.attention_fp8_rows(qc, qs, kc, ks, vc, vs, scale, rows, causal=causal)
     Qd, Kd, Vd = (ofp8.dequantize_blocks(c, s) for c, s in ((qc, qs), (kc, ks), (vc, vs)))
-    o_bound, dS = _fp8_bound(Qd, Kd, Vd, vc, vs, scale, rows)
+    o_bound, dS = _fp8_bound(Qd, Kd, Vd, vc, vs, scale, rows, causal)
     bound = o_bound + half_ulp(O_ref, out_dtype)
     assert np.isfinite(O).all() and np.isfinite(L).all(), f"{what}: non-finite output"
     err = np.abs(O - O_ref)
@@ -139,6 +141,31 @@ def test_fp8_forward_parity(gpu_lib, in_dtype, out_dtype, d, N):
                                   np.arange(N), f"N={N} d={d} h={h}")
         worst = max(worst, frac)
     print(f"N={N} d={d} {out_dtype}: worst error / bound = {worst:.3f}")
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 2, 65, 127, 128, 129, 300, 1000])
+def test_fp8_causal_parity(gpu_lib, out_dtype, d, N):
+    """fa_fwd_fp8_causal against causal attention of the dequantised tensors: query blocks
+    of 128 rows and key tiles of 64 put the diagonal inside, at and across tile edges."""
+    B, H = 2, 2
+    in_dtype = "bf16"
+    q, k, v = (wl.random_tensor((B, H, N, d), in_dtype, [N, d, t, 7]) for t in (1, 2, 3))
+    v[1, 0, : min(N, 40)] *= 16.0
+    v = wl.round_to_dtype(v, in_dtype)
+    O, L = _run_fp8(gpu_lib, q, k, v, in_dtype, out_dtype, causal=True)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            e, frac, le = _check_head(O[b, h], L[b, h], q[b, h], k[b, h], v[b, h], scale_of(d), out_dtype,
+                                      np.arange(N), f"causal N={N} d={d} b={b} h={h}", causal=True)
+            worst = max(worst, frac)
+    # row 0 attends to key 0 alone: P = 2^1 is exact in E4M3, so O_0 is V^_0 rounded once
+    vc, vs = ofp8.quantize_blocks(v[0, 0])
+    v0 = ofp8.dequantize_blocks(vc, vs)[0]
+    assert (np.abs(O[0, 0, 0] - v0) <= 1e-6 * np.abs(v0) + half_ulp(v0, out_dtype)).all()
+    print(f"causal N={N} d={d} {out_dtype}: worst error / bound = {worst:.3f}")
 
 
 def test_fp8_edge_workload_closed_forms(gpu_lib):
@@ -185,6 +212,28 @@ def test_fp8_large_sampled(gpu_lib, B, H, N):
         e, frac, le = _check_head(to_host(o[b, h])[rows], lse[b, h].cpu().numpy().astype(np.float64)[rows],
                                   qh, kh, vh, scale_of(d), "bf16", rows, f"B={B} H={H} N={N} b={b} h={h}")
         print(f"N={N} b={b} h={h}: max err {e:.2e}, worst error / bound {frac:.3f}, LSE err {le:.1e}")
+
+
+def test_fp8_causal_large_sampled(gpu_lib):
+    """The causal kernel on the long-sequence grid, sampled rows near the start, at block
+    and tile edges and at the end."""
+    import torch
+
+    B, H, N, d = 2, 16, 16384, 128
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    q, k, v = (torch.randn(B, H, N, d, device="cuda", dtype=torch.bfloat16, generator=gen) for _ in range(3))
+    q8, qs = gpu_lib.fa_quantize_fp8(q)
+    k8, ks = gpu_lib.fa_quantize_fp8(k)
+    vt8, vs = gpu_lib.fa_quantize_fp8(v, transpose=True)
+    o, lse = gpu_lib.fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.array(sorted({0, 1, 63, 64, 127, 128, 8191, N - 1} | set(rng.choice(N, 24, replace=False).tolist())))
+    for (b, h) in ((0, 0), (B - 1, H - 1)):
+        qh, kh, vh = (to_host(t[b, h]) for t in (q, k, v))
+        e, frac, le = _check_head(to_host(o[b, h])[rows], lse[b, h].cpu().numpy().astype(np.float64)[rows],
+                                  qh, kh, vh, scale_of(d), "bf16", rows, f"causal N={N} b={b} h={h}", causal=True)
+        print(f"causal N={N} b={b} h={h}: max err {e:.2e}, worst error / bound {frac:.3f}, LSE err {le:.1e}")
 
 
 def test_fp8_deterministic_and_empty(gpu_lib):

@@ -153,6 +153,31 @@ def test_attention_fp8_is_attention_of_the_dequantised_tensors():
     np.testing.assert_allclose(Lr, L[rows], atol=1e-13)
 
 
+def test_attention_fp8_causal_closed_forms():
+    """Causal fp8 attention: row 0 sees only key 0 (O = V^_0, LSE = its one score), the
+    last row sees every key (the non-causal row), and row i matches attention over the
+    first i + 1 dequantised keys alone."""
+    rng = np.random.default_rng(10)
+    Q, K, V = (rng.standard_normal((130, 16)) for _ in range(3))
+    (qc, qs), (kc, ks), (vc, vs) = (fp8.quantize_blocks(x) for x in (Q, K, V))
+    Qd, Kd, Vd = (fp8.dequantize_blocks(c, s) for c, s in ((qc, qs), (kc, ks), (vc, vs)))
+    O, L = fp8.attention_fp8(qc, qs, kc, ks, vc, vs, 0.3, causal=True)
+    np.testing.assert_array_equal(O[0], Vd[0])
+    assert abs(L[0] - 0.3 * float(Qd[0] @ Kd[0])) < 1e-14
+    Of, Lf = fp8.attention_fp8(qc, qs, kc, ks, vc, vs, 0.3)
+    np.testing.assert_allclose(O[-1], Of[-1], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(L[-1], Lf[-1], rtol=0, atol=1e-14)
+    for i in (1, 63, 64, 100):
+        S = 0.3 * (Kd[: i + 1] @ Qd[i])
+        w = np.exp(S - S.max())
+        np.testing.assert_allclose(O[i], (w / w.sum()) @ Vd[: i + 1], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(L[i], S.max() + np.log(w.sum()), rtol=0, atol=1e-13)
+    rows = np.array([0, 5, 64, 129])
+    Or, Lr = fp8.attention_fp8_rows(qc, qs, kc, ks, vc, vs, 0.3, rows, causal=True)
+    np.testing.assert_allclose(Or, O[rows], atol=1e-13)
+    np.testing.assert_allclose(Lr, L[rows], atol=1e-13)
+
+
 # ------------------------------------------------------------------ mutations ---
 
 def _mutant(old, new):
