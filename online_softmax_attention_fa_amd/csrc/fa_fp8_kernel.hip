@@ -50,8 +50,10 @@ __device__ __forceinline__ f32x16 mma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 // Four fp32 values to E4M3 codes, round to nearest even; value i lands in byte i.
-__device__ __forceinline__ unsigned pack4_fp8(float x0, float x1, float x2, float x3) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+__device__ __forceinline__ unsigned pack4_fp8(float x0, float x1, float x2, float x3, int old = 0) {
+    // the first conversion fills bytes 0-1 and the second bytes 2-3, so the word's
+    // starting contents (`old`) never matter; passing a dead register saves initialising one
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, old, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
     return (unsigned)w;
 }
@@ -280,6 +282,10 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
     };
 
     f32x16 o[DB];
+    // P codes of the current 64-key step, the B operand of O^T += V^T P^T: dword 2q + kk
+    // holds word q of 32-key block kk (kept across steps so the codes overwrite the last
+    // step's in place)
+    i32x8 pb = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -343,7 +349,6 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
         // own maximum when a lane's sum of P over it leaves range.
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            unsigned pk[2][4];
             float tsum;
             auto make_p = [&](float neg_m) {
                 const float nm = neg_m + vsh_e[ks];
@@ -356,7 +361,8 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
 #pragma unroll
                     for (int t = 0; t < 16; t += 2) { acc0 += p[t]; acc1 += p[t + 1]; }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) pk[kk][q] = pack4_fp8(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
+                    for (int q = 0; q < 4; ++q)
+                        pb[2 * q + kk] = (int)pack4_fp8(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3], pb[2 * q + kk]);
                 }
                 tsum = (acc0 + acc1) * vw[ks];
             };
@@ -387,14 +393,13 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
             // lanes 0-31 keep block 2ks's codes and take block 2ks+1's from lanes 32-63
             // (and the reverse), interleaved so that dword i holds keys 4i .. 4i+3 of the
             // lane's 32, the order of V^T in LDS
-            unsigned pbw[8];
+            // (swapped in place: the pair stays in the operand's registers)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const auto r = __builtin_amdgcn_permlane32_swap(pk[0][q], pk[1][q], false, false);
-                pbw[2 * q] = r[0];
-                pbw[2 * q + 1] = r[1];
+                const auto r = __builtin_amdgcn_permlane32_swap((unsigned)pb[2 * q], (unsigned)pb[2 * q + 1], false, false);
+                pb[2 * q] = (int)r[0];
+                pb[2 * q + 1] = (int)r[1];
             }
-            const i32x8 pb = {(int)pbw[0], (int)pbw[1], (int)pbw[2], (int)pbw[3], (int)pbw[4], (int)pbw[5], (int)pbw[6], (int)pbw[7]};
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const u32x4 n0 = lds_read16(sbase, voff[ks][0] + db * 32 * RV);
