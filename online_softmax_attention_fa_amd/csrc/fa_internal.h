@@ -99,6 +99,12 @@ inline int fwd_lds_bytes(int dtype, int d, int block_k) {
 //    causal grid mixes long and short query blocks and its diagonal tiles carry masking
 //    work; the third wave hides those stalls (4% faster at B=4 H=32 N=16384, while the
 //    non-causal kernel is 2.6% slower this way).
+//  * Non-causal d = 128 on the 4-wave plan, when three workgroups per CU take fewer
+//    rounds x workgroups-per-CU than two (e.g. 528 or 640 workgroups, just over one round
+//    of 512): Bc = 32 and three workgroups per CU, so the grid runs as one round instead of
+//    a full round and a nearly empty one (8% faster at B=2 H=8 N=4097 and B=5 H=8 N=2048).
+//    Causal grids are left alone: their workgroups differ in length, and there the same
+//    switch measured 8-21% slower.
 // fp32: 32 query rows per workgroup, its 4 waves splitting the 32-key tiles among
 // themselves (latency-bound sizes only).
 inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal) {
@@ -118,6 +124,11 @@ inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int d
         if (eight && causal && d == 128) {   // see above: three waves per SIMD
             p.waves = 4;
             p.block_k = 32;
+        }
+        if (!eight && !causal && d == 128) {
+            // rounds x workgroups per CU, in units of one 128-row workgroup's work
+            const int64_t g4 = B * H * ceil_div(N, 4 * 32);
+            if (ceil_div(g4, 3 * kCus) * 3 < ceil_div(g4, 2 * kCus) * 2) p.block_k = 32;
         }
     }
     p.block_q = p.waves * p.rows_per_wave / p.wave_kv_splits;

@@ -188,6 +188,31 @@ def test_eight_wave_plan_sampled(gpu_lib, dtype, d, N, causal):
     assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("B,H,N", [(5, 8, 2001), (2, 8, 4097)])
+def test_three_per_cu_plan_sampled(gpu_lib, dtype, B, H, N):
+    # grids just over one round of two 128-row workgroups per CU run on the 32-key-tile
+    # kernel at three per CU (non-causal); ragged last query block and key tile
+    import torch
+
+    d = 128
+    plan = gpu_lib.fa_fwd_plan(B, H, N, d, wl_dtype_code(dtype))
+    assert plan["waves"] == 4 and plan["block_k"] == 32
+    q, k, v = _random_qkv(B, H, N, d, dtype, seed=N + B)
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    o, lse = gpu_lib.fa_fwd(tq, tk, tv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng([N, B])
+    for b, h in ((0, 0), (B - 1, H - 1), (B // 2, 3)):
+        rows = np.unique(np.concatenate([[0, 31, 32, 127, 128, N - 129, N - 128, N - 1], rng.choice(N, 40, replace=False)]))
+        rows = rows[(rows >= 0) & (rows < N)]
+        rr = torch.from_numpy(rows).cuda()
+        Og = to_host(o[b, h].index_select(0, rr))
+        Lg = lse[b, h].index_select(0, rr).cpu().numpy().astype(np.float64)
+        O_ref, L_ref = attention_rows(q[b, h], k[b, h], v[b, h], scale_of(d), rows)
+        compare(Og, Lg, O_ref, L_ref, dtype, f"B{B} H{H} N={N} {dtype} b{b} h{h}")
+
+
 def wl_dtype_code(dtype):
     import online_softmax_attention_fa_amd as fa
 
