@@ -157,22 +157,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
                 s[kb] = Elt<T>::mma(lds_read16(sbase, koff[ds] + kb * 32 * RB), qf[ds], s[kb]);
                 dp[kb] = Elt<T>::mma(lds_read16(sbase, TILE + koff[ds] + kb * 32 * RB), dof[ds], dp[kb]);
             }
+        // masks in a branch of their own (uniform per wave), so full tiles run none of it
         const bool tail = kbase + BC > N;
         const bool diag = CAUSAL && (kbase + BC - 1 > q_wave);
+        if (tail || diag) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const int key = kbase + kb * 32 + 8 * (t >> 2) + 4 * h + (t & 3);
+                    bool drop = key >= N;
+                    if (CAUSAL) drop = drop || key > query;
+                    if (drop) s[kb][t] = -INFINITY;
+                }
+        }
         u32x4 dsf[KS];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             float v[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                float x = s[kb][t];
-                if (tail || diag) {
-                    const int key = kbase + kb * 32 + 8 * (t >> 2) + 4 * h + (t & 3);
-                    bool drop = key >= N;
-                    if (CAUSAL) drop = drop || key > query;
-                    if (drop) x = -INFINITY;
-                }
-                const float p = fast_exp2(__builtin_fmaf(x, c, -l2));
+                const float p = fast_exp2(__builtin_fmaf(s[kb][t], c, -l2));
                 v[t] = p * (dp[kb][t] - dd);
             }
 #pragma unroll
@@ -373,8 +378,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         // Phase fences: keep the scheduler from hoisting one phase's LDS reads into the
         // previous one, which overruns the register budget.
         __builtin_amdgcn_sched_barrier(0);
+        // masks in a branch of their own (uniform per wave), so full tiles run none of it
         const bool tail = qbase + BQ > N;
         const bool diag = CAUSAL && (k_wave + KPW - 1 > qbase);
+        if (tail || diag) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const int q = qbase + qb * 32 + 8 * (t >> 2) + 4 * h + (t & 3);
+                    bool drop = q >= N;
+                    if (CAUSAL) drop = drop || key > q;
+                    if (drop) s[qb][t] = -INFINITY;
+                }
+        }
         const lds_f32* l2t = (const lds_f32*)(sbase + 2 * TILE);
         const lds_f32* ddt = (const lds_f32*)(sbase + 2 * TILE + 64 * 4);
         u32x4 pfb[QS], dsb[QS];
@@ -389,14 +406,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 4 * g + e;
-                    float x = s[qb][t];
-                    if (tail || diag) {
-                        const int q = qbase + r0 + e;
-                        bool drop = q >= N;
-                        if (CAUSAL) drop = drop || key > q;
-                        if (drop) x = -INFINITY;
-                    }
-                    const float p = fast_exp2(__builtin_fmaf(x, c, -l4[e]));
+                    const float p = fast_exp2(__builtin_fmaf(s[qb][t], c, -l4[e]));
                     pv[t] = p;
                     dsv[t] = p * (dp[qb][t] - d4[e]);
                 }
