@@ -58,3 +58,57 @@ def test_forward_splitkv_backward_in_one_graph(gpu_lib):
         torch.cuda.synchronize()
         for name, t, r in zip(("o", "lse", "o_split", "lse_split", "dq", "dk", "dv"), outs, ref):
             assert torch.equal(t.view(torch.int8), r.view(torch.int8)), f"replay {rep}: {name} differs"
+
+
+def test_fp8_and_causal_in_one_graph(gpu_lib):
+    """The fp8 quantiser (including V^T's zero padding) and the fp8 and 16-bit causal
+    forwards, captured together and replayed with the outputs poisoned in between."""
+    import torch
+
+    fa = gpu_lib
+    B, H, N, d = 2, 3, 333, 64
+    gen = torch.Generator(device="cuda").manual_seed(32)
+    q, k, v = (torch.randn(B, H, N, d, device="cuda", dtype=torch.bfloat16, generator=gen) for _ in range(3))
+    Np, nb = fa.fa_fp8_padded_len(N), fa.fa_fp8_scale_blocks(N)
+    q8, k8 = (torch.empty(B, H, N, d, dtype=torch.uint8, device="cuda") for _ in range(2))
+    vt8 = torch.empty(B, H, d, Np, dtype=torch.uint8, device="cuda")
+    qs, ks, vs = (torch.empty(B, H, nb, dtype=torch.float32, device="cuda") for _ in range(3))
+    o8, o8c, oc = (torch.empty_like(q) for _ in range(3))
+    l8, l8c, lc = (torch.empty(B, H, N, device="cuda", dtype=torch.float32) for _ in range(3))
+
+    def work(stream):
+        fa.fa_quantize_fp8(q, x8=q8, scales=qs, stream=stream)
+        fa.fa_quantize_fp8(k, x8=k8, scales=ks, stream=stream)
+        fa.fa_quantize_fp8(v, transpose=True, x8=vt8, scales=vs, stream=stream)
+        fa.fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, o8, l8, stream=stream)
+        fa.fa_fwd_fp8(q8, k8, vt8, qs, ks, vs, o8c, l8c, stream=stream, causal=True)
+        fa.fa_fwd(q, k, v, oc, lc, causal=True, stream=stream)
+
+    work(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    outs = (q8, k8, vt8, qs, ks, vs, o8, l8, o8c, l8c, oc, lc)
+    ref = [t.clone() for t in outs]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work(torch.cuda.current_stream())
+
+    names = ("q8", "k8", "vt8", "qs", "ks", "vs", "o_fp8", "lse_fp8", "o_fp8_causal", "lse_fp8_causal",
+             "o_causal", "lse_causal")
+    for rep in range(4):
+        for t in outs:
+            if t.dtype == torch.uint8:
+                t.fill_(0x7F)          # a NaN code, and non-zero in V^T's padding
+            else:
+                t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(names, outs, ref):
+            assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}: {name} differs"
