@@ -23,6 +23,9 @@ ONE JSON line on stdout (everything else goes to stderr):
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload (whole heads
              in row chunks, all keys, about 15 s of host time), timed on the host
              cores, with the GPU output checked on the same rows
+  power      socket power and GFX clock (amd-smi) sampled while the forward runs back to back
+             for --power-seconds after the timed steps, with the board's power cap; the
+             kernel is power-bound on this workload, so these numbers bound its rate
   sweep      (--sweep only) forward time of the smaller workloads (fp32 B1 H1 N256 d64,
              bf16 B4 H16 N2048 d64, fp16 B1 H32 N16384 d128, bf16 B2 H8 N4097 d128), the
              causal and split-KV variants, the fp8 forward causal at d=128 and at d=64,
@@ -196,6 +199,71 @@ def time_fp8(fa, q, k, v, o_ref, scale, stream, steps):
             "outputs_finite": ok, "steps": steps}
 
 
+def _smi(cmd):
+    import subprocess
+
+    try:
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=20)
+        return r.stdout
+    except (OSError, subprocess.SubprocessError):
+        return ""
+
+
+def parse_smi_metric(txt):
+    """(socket watts, mean GFX MHz over the XCDs) from `amd-smi metric -p -c` text, or None."""
+    w = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+    clk = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", txt)]
+    if not w or not clk:
+        return None
+    return float(w[0]), sum(clk) / len(clk)
+
+
+def power_while_running(fn, seconds, settle=1.0, period=0.25):
+    """Socket power (W) and per-XCD GFX clocks (MHz) from `amd-smi metric -p -c`, sampled in a
+    child process while `fn` (one forward launch) runs back to back for `seconds`.  Samples in
+    the first `settle` seconds are dropped (clocks and power ramp up).  None if amd-smi is absent."""
+    import threading
+
+    import torch
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            t = time.perf_counter()
+            got = parse_smi_metric(_smi(["amd-smi", "metric", "-g", "0", "-p", "-c"]))
+            if got is not None:
+                samples.append((t, *got))
+            stop.wait(period)
+
+    cap_txt = _smi(["rocm-smi", "--showmaxpower"])
+    cap = re.findall(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", cap_txt)
+    fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    kept = [s for s in samples if s[0] - t0 >= settle]
+    if not kept:
+        return None
+    watts = [s[1] for s in kept]
+    mhz = [s[2] for s in kept]
+    return {"socket_w_mean": round(sum(watts) / len(watts), 1), "socket_w_max": round(max(watts), 1),
+            "power_cap_w": float(cap[0]) if cap else None,
+            "gfx_mhz_mean": round(sum(mhz) / len(mhz), 1), "samples": len(kept),
+            "seconds": round(wall, 2), "launches": n, "ms_per_launch": round(wall * 1e3 / n, 4),
+            "source": "amd-smi metric -p -c (socket power, mean GFX clock of the 8 XCDs); rocm-smi --showmaxpower"}
+
+
 def launch_times(fn, stream, steps, warmup=5):
     """Per-launch durations (ms) from events recorded between back-to-back launches."""
     import torch
@@ -305,6 +373,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time the smaller workloads")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--fp8-steps", type=int, default=10)
+    ap.add_argument("--power-seconds", type=float, default=4.0,
+                    help="run the forward this long while sampling socket power and clock (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -398,6 +468,14 @@ def main():
             "traffic": traffic,
         },
     }
+    if args.power_seconds > 0:
+        pw = power_while_running(lambda: fa.fa_fwd(q, k, v, o, lse, scale=scale, stream=stream), args.power_seconds)
+        if pw is not None:
+            # the same FLOPs against the MFMA peak at the clock the chip actually ran
+            pw["frac_of_peak_at_measured_clock"] = round(
+                achieved / (PEAK_BF16_TFLOPS * pw["gfx_mhz_mean"] / 2400.0), 4)
+        out["power"] = pw
+        log(f"power: {pw}")
     if not args.no_backward:
         out["backward"] = time_backward(fa, q, k, v, o, lse, scale, stream, args.backward_steps)
     if not args.no_fp8:

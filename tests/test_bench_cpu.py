@@ -46,3 +46,17 @@ def test_counter_summary_is_parsed():
     assert note == "ok"
     # algorithmic bytes of the workload are 2.156e9; traffic cannot be below them
     assert 2.0e9 < traffic < 2.0e10
+
+
+def test_amd_smi_metric_text_is_parsed():
+    import bench
+
+    clocks = (1983, 1883, 1975, 1929, 2005, 1913, 1962, 1909)
+    txt = "GPU: 0\n    POWER:\n        SOCKET_POWER: 1344 W\n        GFX_VOLTAGE: N/A\n    CLOCK:\n"
+    for i, c in enumerate(clocks):
+        txt += f"        GFX_{i}:\n            CLK: {c} MHz\n            MIN_CLK: 500 MHz\n            MAX_CLK: 2400 MHz\n"
+    txt += "        MEM_0:\n            CLK: 2000 MHz\n"
+    watts, mhz = bench.parse_smi_metric(txt)
+    assert watts == 1344.0
+    assert mhz == pytest.approx(sum(clocks) / 8)   # the memory clock is not a GFX clock
+    assert bench.parse_smi_metric("amd-smi: command not found") is None
