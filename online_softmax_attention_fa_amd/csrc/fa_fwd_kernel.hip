@@ -190,18 +190,21 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int t = 0; t < 16; ++t) s[kb][t] = 0.f;
-        // K fragments are read one k-step ahead of the MFMAs that use them
-        u32x4 kf[2][KB];
+        // One 32-key block at a time: its DS k-steps run back to back on one accumulator, so
+        // each MFMA takes the previous one's result as its C operand directly.  Round-robin
+        // over the KB accumulators measured slower (a bare MFMA loop on gfx950 runs at 71%
+        // busy with 2 or 4 interleaved accumulators, 87% with 1 or 8).  K fragments are read
+        // KPF steps ahead; the schedule barriers keep the compiler from interleaving again.
+        constexpr int NQK = KB * DS, KPF = 6;
+        u32x4 kf[KPF + 1];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kf[0][kb] = lds_read16(sbase, koff[0] + kb * 32 * RB);
+        for (int i = 0; i < KPF; ++i) kf[i] = lds_read16(sbase, koff[i % DS] + (i / DS) * 32 * RB);
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-            if (ds + 1 < DS) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) kf[(ds + 1) & 1][kb] = lds_read16(sbase, koff[ds + 1] + kb * 32 * RB);
-            }
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) s[kb] = Elt<T>::mma(kf[ds & 1][kb], qf[ds], s[kb]);
+        for (int i = 0; i < NQK; ++i) {
+            if (i + KPF < NQK)
+                kf[(i + KPF) % (KPF + 1)] = lds_read16(sbase, koff[(i + KPF) % DS] + ((i + KPF) / DS) * 32 * RB);
+            s[i / DS] = Elt<T>::mma(kf[i % (KPF + 1)], qf[i % DS], s[i / DS]);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
@@ -277,15 +280,26 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
 
         // ---- O^T += V_j^T P^T
         if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
+        // (same order: the KS k-steps of one 32-dim block of O^T back to back, V^T fragments
+        // gathered VPF steps ahead)
+        {
+            constexpr int NPV = KS * DB, VPF = 4;
+            auto vread = [&](int i) {
+                const int db = i / KS, ks = i % KS;
                 const u32x2 lo = lds_read_tr(sbase, voff[0][db] + ks * 16 * RB);
                 const u32x2 hi = lds_read_tr(sbase, voff[1][db] + ks * 16 * RB);
-                const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-                o[db] = Elt<T>::mma(vf, pf[ks], o[db]);
+                return u32x4{lo[0], lo[1], hi[0], hi[1]};
+            };
+            u32x4 vf[VPF + 1];
+#pragma unroll
+            for (int i = 0; i < VPF; ++i) vf[i] = vread(i);
+#pragma unroll
+            for (int i = 0; i < NPV; ++i) {
+                if (i + VPF < NPV) vf[(i + VPF) % (VPF + 1)] = vread(i + VPF);
+                o[i / KS] = Elt<T>::mma(vf[i % (VPF + 1)], pf[i % KS], o[i / KS]);
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
         if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     };
 
