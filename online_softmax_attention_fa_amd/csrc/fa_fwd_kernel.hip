@@ -57,7 +57,7 @@ namespace fa {
 // so if lane r of the group addresses V[k0 + r/4][d0 + 4(r%4) .. +3], lane c gets
 // V[k0 + e][d0 + c] for e = 0..3: four keys of its own column.
 
-template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool SPLIT = false>
+template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool SPLIT = false, bool PP = false>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource types exist only in the device pass
     constexpr int NT = 64 * WAVES, QPW = 32, BR = WAVES * QPW;
@@ -72,6 +72,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
     constexpr int LOADS = TILE / (NT * 16);   // direct loads per thread per tile, K or V
     static_assert(LOADS >= 1 && TILE % (NT * 16) == 0, "tile must be whole 4 KiB blocks");
     static_assert(!(SPLIT && CAUSAL), "split-KV is non-causal");
+    static_assert(!PP || (WAVES == 8 && !CAUSAL && !SPLIT), "ping-pong: 8 waves, non-causal");
 
     // Two stages in two separate arrays: the compiler can then prove that the copies
     // into one stage do not alias the reads of the other and adds no wait for them.
@@ -79,12 +80,20 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
     __shared__ __attribute__((aligned(1024))) unsigned char stage1_raw[STAGE];
     lds_u8* const stage0 = (lds_u8*)stage0_raw;
     lds_u8* const stage1 = (lds_u8*)stage1_raw;
+    lds_u8* stage2 = nullptr;   // third stage of the ping-pong schedule
+    if constexpr (PP) {
+        __shared__ __attribute__((aligned(1024))) unsigned char stage2_raw[STAGE];
+        stage2 = (lds_u8*)stage2_raw;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
     const int h = lane >> 5, l32 = lane & 31;
-    const int N = a.n, NK = a.nk;   // query rows, keys (equal unless a split-KV call differs)
+    const int N = a.n, NK = a.nk;
+    // ping-pong: waves w and w + 4 share a SIMD (the dispatcher deals a workgroup's waves
+    // round-robin over its four SIMDs); the late group runs half a tile behind the early one
+    const bool late = PP && wave >= 4;   // query rows, keys (equal unless a split-KV call differs)
 
     const int bid = remap_xcd(blockIdx.x, a.n_blocks);
     // split-KV: the splits of one query block are neighbours in the grid (same XCD, L2)
@@ -177,7 +186,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
         n_tiles = min(n_tiles, t0 + a.tiles_per_split);
     }
 
-    auto compute_tile = [&](int j, const lds_u8* sbase) {
+    u32x4 pf[KS];   // P of the current tile, packed: the B operand of O^T += V^T P^T
+    // S, the masks, P and the row sums of tile j
+    auto qk_soft = [&](int j, const lds_u8* sbase) __attribute__((always_inline)) {
         const int kbase = j * BC;
         // MFMA-heavy stretches run at raised wave priority, so the SIMD issues them ahead of
         // the other wave's VALU work (measured 0.4-3% faster in every variant).
@@ -226,7 +237,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
         // does not depend on m, which only has to keep P finite and in range.  A tile is
         // redone with its own maximum when some row's tile sum leaves [0, 2^15] -- the first
         // tile (m = -inf), or a row maximum that jumped by more than 15 in base-2 units.
-        u32x4 pf[KS];
         float acc0, acc1, racc0, racc1;
         auto make_p = [&](float neg_m) {
             acc0 = 0.f, acc1 = 0.f, racc0 = 0.f, racc1 = 0.f;
@@ -275,8 +285,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
         }
         lsum += acc0 + acc1;
         lrnd += racc0 + racc1;
-
-        // ---- O^T += V_j^T P^T
+    };
+    // O^T += V_j^T P^T
+    auto pv = [&](const lds_u8* sbase) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
         // (same order: the KS k-steps of one 32-dim block of O^T back to back, V^T fragments
         // gathered VPF steps ahead)
@@ -300,23 +311,65 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
         }
         __builtin_amdgcn_s_setprio(0);
     };
+    auto compute_tile = [&](int j, const lds_u8* sbase) __attribute__((always_inline)) {
+        qk_soft(j, sbase);
+        pv(sbase);
+    };
 
-    if (t0 < n_tiles) issue_tile(t0, stage0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's LDS copies have landed
-    __syncthreads();
-
-    for (int j = t0; j < n_tiles; j += 2) {
-        // stage 0 holds tile j; tile j + 1 streams into stage 1 meanwhile
-        if (j + 1 < n_tiles) issue_tile(j + 1, stage1);
-        if (!CAUSAL || j * BC <= q_wave + QPW - 1) compute_tile(j, stage0);
+    // Ping-pong schedule (d = 64, where the softmax takes longer than the MFMAs): every wave
+    // runs qk_soft(j) then pv(j) per tile, but the two groups take the tile barrier at
+    // different points -- the early group after pv(j), the late group between qk_soft(j) and
+    // pv(j).  Each wave passes one barrier per tile, and a barrier event pairs the early
+    // group's end of tile j with the late group's middle of tile j, so the late group runs
+    // half a tile behind and each group's MFMAs fall in the other's softmax.
+    // Stages: tile j + 1 is copied, at the start of step j, into the stage of tile j - 2; both
+    // groups are done with it by then (the late group's last read, V of tile j - 2, comes
+    // before the barrier that ends its step j - 1).  So three stages, the loop unrolled by
+    // three to keep every stage a distinct array at compile time.
+    auto pp_step = [&](int j, const lds_u8* cur) __attribute__((always_inline)) {
+        qk_soft(j, cur);
+        if (late) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's copies have landed
+            __syncthreads();
+        }
+        pv(cur);
+        if (!late) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+        }
+    };
+    if constexpr (PP) {
+        if (t0 < n_tiles) issue_tile(t0, stage0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        if (j + 1 >= n_tiles) break;
-        // stage 1 holds tile j + 1
-        if (j + 2 < n_tiles) issue_tile(j + 2, stage0);
-        if (!CAUSAL || (j + 1) * BC <= q_wave + QPW - 1) compute_tile(j + 1, stage1);
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+        for (int j = t0; j < n_tiles; j += 3) {
+            if (j + 1 < n_tiles) issue_tile(j + 1, stage1);
+            pp_step(j, stage0);
+            if (j + 1 >= n_tiles) break;
+            if (j + 2 < n_tiles) issue_tile(j + 2, stage2);
+            pp_step(j + 1, stage1);
+            if (j + 2 >= n_tiles) break;
+            if (j + 3 < n_tiles) issue_tile(j + 3, stage0);
+            pp_step(j + 2, stage2);
+        }
+    } else {
+        if (t0 < n_tiles) issue_tile(t0, stage0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's LDS copies have landed
         __syncthreads();
+
+        for (int j = t0; j < n_tiles; j += 2) {
+            // stage 0 holds tile j; tile j + 1 streams into stage 1 meanwhile
+            if (j + 1 < n_tiles) issue_tile(j + 1, stage1);
+            if (!CAUSAL || j * BC <= q_wave + QPW - 1) compute_tile(j, stage0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+            if (j + 1 >= n_tiles) break;
+            // stage 1 holds tile j + 1
+            if (j + 2 < n_tiles) issue_tile(j + 2, stage0);
+            if (!CAUSAL || (j + 1) * BC <= q_wave + QPW - 1) compute_tile(j + 1, stage1);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: O / l, LSE = (m + log2 l) ln 2
@@ -593,7 +646,12 @@ static hipError_t launch_t(const FwdArgs& a, int causal, hipStream_t st) {
 template <typename T>
 static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int causal, hipStream_t st) {
     if (d == 128 && p.block_k == 128 && p.waves == 8) return launch_t<T, 128, 128, 8>(a, causal, st);
-    if (d == 64 && p.block_k == 128 && p.waves == 8) return launch_t<T, 64, 128, 8>(a, causal, st);
+    if (d == 64 && p.block_k == 128 && p.waves == 8) {
+        if (causal) return launch_t<T, 64, 128, 8>(a, causal, st);
+        // non-causal d = 64 on the ping-pong schedule
+        hipLaunchKernelGGL((fwd_kernel<T, 64, 128, 8, false, false, true>), dim3((unsigned)a.n_blocks), dim3(512), 0, st, a);
+        return hipGetLastError();
+    }
     if (d == 128 && p.block_k == 64 && p.waves == 4) return launch_t<T, 128, 64, 4>(a, causal, st);
     if (d == 64 && p.block_k == 128 && p.waves == 4) return launch_t<T, 64, 128, 4>(a, causal, st);
     if (d == 128 && p.block_k == 32 && p.waves == 4) return launch_t<T, 128, 32, 4>(a, causal, st);
