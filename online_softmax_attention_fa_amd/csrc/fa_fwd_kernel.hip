@@ -90,10 +90,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
     const int h = lane >> 5, l32 = lane & 31;
-    const int N = a.n, NK = a.nk;
+    const int N = a.n, NK = a.nk;   // query rows, keys (equal unless a split-KV call differs)
     // ping-pong: waves w and w + 4 share a SIMD (the dispatcher deals a workgroup's waves
     // round-robin over its four SIMDs); the late group runs half a tile behind the early one
-    const bool late = PP && wave >= 4;   // query rows, keys (equal unless a split-KV call differs)
+    const bool late = PP && wave >= 4;
 
     const int bid = remap_xcd(blockIdx.x, a.n_blocks);
     // split-KV: the splits of one query block are neighbours in the grid (same XCD, L2)
