@@ -48,7 +48,9 @@ namespace fa {
 // softmax VALU work overlaps the other's MFMAs.  K/V tiles of BC keys are copied
 // HBM -> LDS with buffer_load_dwordx4 ... lds (no staging registers), two stages, one
 // barrier per tile.  Rows past N read as zeros (buffer range check) and
-// their scores are masked to -inf, so they contribute exactly 0.
+// their scores are masked to -inf, so they contribute exactly 0.  PP (8 waves,
+// non-causal d = 64) selects the ping-pong schedule described at its loop: three stages,
+// the two waves of each SIMD half a tile apart.
 //
 // V operand of O^T += V^T P^T: lane L needs V[key][d] for d = 32db + L%32 and the 8
 // keys the P^T accumulator registers of lane L hold.  V stays row-major in LDS and
