@@ -105,6 +105,11 @@ inline int fwd_lds_bytes(int dtype, int d, int block_k) {
 //    a full round and a nearly empty one (8% faster at B=2 H=8 N=4097 and B=5 H=8 N=2048).
 //    Causal grids are left alone: their workgroups differ in length, and there the same
 //    switch measured 8-21% slower.
+//  * Non-causal d = 128 with N < 2048 and at least two workgroups of 128 rows per CU: the
+//    same 32-key plan.  Short heads are bound by latency and HBM, and a third resident
+//    workgroup per CU overlaps one's copies with another's compute (B=16 H=64: N=128 35 ->
+//    31 us, N=640 -3%, N=1024 -3%, N=2047 -0.7%).  Smaller grids keep Bc = 64 (at 64
+//    workgroups the 32-key plan measured up to 3% slower).
 // fp32: 32 query rows per workgroup, its 4 waves splitting the 32-key tiles among
 // themselves (latency-bound sizes only).
 inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal) {
@@ -129,6 +134,7 @@ inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int d
             // rounds x workgroups per CU, in units of one 128-row workgroup's work
             const int64_t g4 = B * H * ceil_div(N, 4 * 32);
             if (ceil_div(g4, 3 * kCus) * 3 < ceil_div(g4, 2 * kCus) * 2) p.block_k = 32;
+            if (N < 2048 && g4 >= 2 * kCus) p.block_k = 32;
         }
     }
     p.block_q = p.waves * p.rows_per_wave / p.wave_kv_splits;

@@ -166,14 +166,20 @@ def test_plan_respects_lds_and_covers_rows(lib, dtype, d):
         assert p["kv_splits"] >= 1
 
 
-def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round(lib):
+def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_short_heads(lib):
     # 528 workgroups of 128 rows: two per CU leave a nearly empty second round, three per
     # CU (32-key tiles) fit them in one; causal grids and full rounds keep 64-key tiles
     p = fa.fa_fwd_plan(2, 8, 4097, 128, fa.FA_BF16)
     assert (p["waves"], p["block_k"], p["grid"]) == (4, 32, 528)
     assert fa.fa_fwd_plan(5, 8, 2048, 128, fa.FA_F16)["block_k"] == 32
     assert fa.fa_fwd_plan(2, 8, 4097, 128, fa.FA_BF16, causal=True)["block_k"] == 64
-    assert fa.fa_fwd_plan(16, 16, 1024, 128, fa.FA_BF16)["block_k"] == 64
+    # short sequences with two or more 128-row workgroups per CU also take 32-key tiles
+    # (latency-bound: a third resident workgroup overlaps copies with compute); a small
+    # grid, or a causal one, keeps 64-key tiles
+    assert fa.fa_fwd_plan(16, 16, 1024, 128, fa.FA_BF16)["block_k"] == 32
+    assert fa.fa_fwd_plan(16, 64, 128, 128, fa.FA_BF16)["block_k"] == 32
+    assert fa.fa_fwd_plan(1, 8, 1024, 128, fa.FA_BF16)["block_k"] == 64
+    assert fa.fa_fwd_plan(16, 16, 1024, 128, fa.FA_BF16, causal=True)["block_k"] == 64
     assert fa.fa_fwd_plan(3, 6, 3000, 128, fa.FA_BF16)["block_k"] == 64
     assert fa.fa_fwd_plan(2, 8, 4097, 64, fa.FA_BF16)["block_k"] == 128
 
