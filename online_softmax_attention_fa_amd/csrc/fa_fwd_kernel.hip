@@ -114,6 +114,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
 
     const int q_wave = qblk * BR + wave * QPW;   // first query row of this wave
     const int query = q_wave + l32;              // the query this lane's columns belong to
+    // A wave whose 32 rows all lie past N (the last query block; one-query decoding) skips
+    // the tile work, not the copies or barriers: its rows are never stored.
+    const bool has_rows = q_wave < N;
     const float c = a.c;
 
     // ---- Q^T fragments (B operand): query row `query`, dims 16s + 8h .. +7
@@ -329,12 +332,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
     // before the barrier that ends its step j - 1).  So three stages, the loop unrolled by
     // three to keep every stage a distinct array at compile time.
     auto pp_step = [&](int j, const lds_u8* cur) __attribute__((always_inline)) {
-        qk_soft(j, cur);
+        if (has_rows) qk_soft(j, cur);
         if (late) {
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's copies have landed
             __syncthreads();
         }
-        pv(cur);
+        if (has_rows) pv(cur);
         if (!late) {
             __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
@@ -362,13 +365,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) vo
         for (int j = t0; j < n_tiles; j += 2) {
             // stage 0 holds tile j; tile j + 1 streams into stage 1 meanwhile
             if (j + 1 < n_tiles) issue_tile(j + 1, stage1);
-            if (!CAUSAL || j * BC <= q_wave + QPW - 1) compute_tile(j, stage0);
+            if (has_rows && (!CAUSAL || j * BC <= q_wave + QPW - 1)) compute_tile(j, stage0);
             __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
             if (j + 1 >= n_tiles) break;
             // stage 1 holds tile j + 1
             if (j + 2 < n_tiles) issue_tile(j + 2, stage0);
-            if (!CAUSAL || (j + 1) * BC <= q_wave + QPW - 1) compute_tile(j + 1, stage1);
+            if (has_rows && (!CAUSAL || (j + 1) * BC <= q_wave + QPW - 1)) compute_tile(j + 1, stage1);
             __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
         }
