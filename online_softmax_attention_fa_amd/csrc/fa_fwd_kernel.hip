@@ -43,9 +43,10 @@ namespace fa {
 
 // ------------------------------------------------------- bf16 / fp16 kernel ---
 //
-// WAVES waves x 32 query rows (Br = 32 WAVES): 4 waves and two workgroups per CU, or
-// 8 waves and one workgroup per CU -- two waves per SIMD either way, so one wave's
-// softmax VALU work overlaps the other's MFMAs.  K/V tiles of BC keys are copied
+// WAVES waves x 32 query rows (Br = 32 WAVES): 4 waves and two workgroups per CU (three
+// with 32-key tiles at d = 128 or 64-key tiles at d = 64), or 8 waves and one workgroup
+// per CU -- two or three waves per SIMD, so one wave's softmax VALU work overlaps
+// another's MFMAs.  K/V tiles of BC keys are copied
 // HBM -> LDS with buffer_load_dwordx4 ... lds (no staging registers), two stages, one
 // barrier per tile.  Rows past N read as zeros (buffer range check) and
 // their scores are masked to -inf, so they contribute exactly 0.  PP (8 waves,
@@ -60,7 +61,7 @@ namespace fa {
 // V[k0 + e][d0 + c] for e = 0..3: four keys of its own column.
 
 template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool SPLIT = false, bool PP = false>
-__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC == 32 ? 3 : 2) : 1) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 2) : 1) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource types exist only in the device pass
     constexpr int NT = 64 * WAVES, QPW = 32, BR = WAVES * QPW;
     constexpr int KB = BC / 32;       // 32-key row blocks of S^T per tile
@@ -659,6 +660,7 @@ static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int cau
     }
     if (d == 128 && p.block_k == 64 && p.waves == 4) return launch_t<T, 128, 64, 4>(a, causal, st);
     if (d == 64 && p.block_k == 128 && p.waves == 4) return launch_t<T, 64, 128, 4>(a, causal, st);
+    if (d == 64 && p.block_k == 64 && p.waves == 4) return launch_t<T, 64, 64, 4>(a, causal, st);
     if (d == 128 && p.block_k == 32 && p.waves == 4) return launch_t<T, 128, 32, 4>(a, causal, st);
     return hipErrorInvalidConfiguration;
 }

@@ -110,6 +110,8 @@ inline int fwd_lds_bytes(int dtype, int d, int block_k) {
 //    workgroup per CU overlaps one's copies with another's compute (B=16 H=64: N=128 35 ->
 //    31 us, N=640 -3%, N=1024 -3%, N=2047 -0.7%).  Smaller grids keep Bc = 64 (at 64
 //    workgroups the 32-key plan measured up to 3% slower).
+//  * The same for d = 64: 64-key tiles (32 KiB of stages, 132 VGPRs), three workgroups per
+//    CU (B=16 H=64: N=128 22 -> 19.5 us, N=512 118 -> 101 us, N=1024 -6%, N=2047 -1.3%).
 // fp32: 32 query rows per workgroup, its 4 waves splitting the 32-key tiles among
 // themselves (latency-bound sizes only).
 inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal) {
@@ -136,6 +138,8 @@ inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int d
             if (ceil_div(g4, 3 * kCus) * 3 < ceil_div(g4, 2 * kCus) * 2) p.block_k = 32;
             if (N < 2048 && g4 >= 2 * kCus) p.block_k = 32;
         }
+        if (!eight && !causal && d == 64 && N < 2048 && B * H * ceil_div(N, 4 * 32) >= 2 * kCus)
+            p.block_k = 64;   // d = 64 short heads: 64-key tiles, three workgroups per CU
     }
     p.block_q = p.waves * p.rows_per_wave / p.wave_kv_splits;
     p.lds_bytes = fwd_lds_bytes(dtype, (int)d, p.block_k);

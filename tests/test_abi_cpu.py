@@ -180,6 +180,11 @@ def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_sh
     assert fa.fa_fwd_plan(16, 64, 128, 128, fa.FA_BF16)["block_k"] == 32
     assert fa.fa_fwd_plan(1, 8, 1024, 128, fa.FA_BF16)["block_k"] == 64
     assert fa.fa_fwd_plan(16, 16, 1024, 128, fa.FA_BF16, causal=True)["block_k"] == 64
+    # d = 64 short heads: 64-key tiles at three per CU; small grids and causal keep 128
+    p = fa.fa_fwd_plan(16, 64, 512, 64, fa.FA_BF16)
+    assert (p["waves"], p["block_k"], p["lds_bytes"]) == (4, 64, 32768)
+    assert fa.fa_fwd_plan(1, 8, 512, 64, fa.FA_BF16)["block_k"] == 128
+    assert fa.fa_fwd_plan(16, 64, 512, 64, fa.FA_BF16, causal=True)["block_k"] == 128
     assert fa.fa_fwd_plan(3, 6, 3000, 128, fa.FA_BF16)["block_k"] == 64
     assert fa.fa_fwd_plan(2, 8, 4097, 64, fa.FA_BF16)["block_k"] == 128
 

@@ -141,6 +141,28 @@ def test_large_magnitude_scores_eight_wave_plans(gpu_lib, dtype, d):
     assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_short_heads_three_per_cu_plan(gpu_lib, dtype, d):
+    # Many short heads (N = 300: four full 64-key tiles and a ragged one) take the
+    # three-workgroups-per-CU plan: 64-key tiles at d = 64, 32-key tiles at d = 128.
+    import torch
+
+    B, H, N = 16, 32, 300
+    plan = gpu_lib.fa_fwd_plan(B, H, N, d, wl_dtype_code(dtype))
+    assert plan["waves"] == 4 and plan["block_k"] == (64 if d == 64 else 32)
+    q, k, v = _random_qkv(B, H, N, d, dtype, seed=300 + d)
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    o, lse = gpu_lib.fa_fwd(tq, tk, tv)
+    torch.cuda.synchronize()
+    for b in range(0, B, 5):
+        for h in range(0, H, 7):
+            O_ref, L_ref = attention_forward(q[b, h], k[b, h], v[b, h], scale_of(d))
+            compare(to_host(o[b, h]), lse[b, h].cpu().numpy().astype(np.float64), O_ref, L_ref, dtype,
+                    f"short heads {dtype} d{d} b{b} h{h}")
+    assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
+
+
 def test_custom_scale_and_stream(gpu_lib):
     import torch
 
