@@ -112,3 +112,50 @@ def test_fp8_and_causal_in_one_graph(gpu_lib):
         torch.cuda.synchronize()
         for name, t, r in zip(names, outs, ref):
             assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}: {name} differs"
+
+
+def test_ping_pong_and_short_head_forwards_in_one_graph(gpu_lib):
+    """The d = 64 ping-pong schedule (8-wave plan, three stages) and the three-per-CU
+    short-head plans (d = 64 and d = 128) captured together; every replay must reproduce
+    the eager results bit for bit."""
+    import torch
+
+    fa = gpu_lib
+    gen = torch.Generator(device="cuda").manual_seed(37)
+    shapes = ((4, 16, 2100, 64), (16, 32, 300, 64), (16, 32, 300, 128))
+    plans = [fa.fa_fwd_plan(*sh, torch.bfloat16) for sh in shapes]
+    assert (plans[0]["waves"], plans[0]["block_k"]) == (8, 128)
+    assert (plans[1]["waves"], plans[1]["block_k"]) == (4, 64)
+    assert (plans[2]["waves"], plans[2]["block_k"]) == (4, 32)
+    ins = [tuple(torch.randn(*sh, device="cuda", dtype=torch.bfloat16, generator=gen) for _ in range(3))
+           for sh in shapes]
+    outs = [(torch.empty_like(q), torch.empty(q.shape[:3], device="cuda", dtype=torch.float32)) for q, _, _ in ins]
+
+    def work(stream):
+        for (q, k, v), (o, lse) in zip(ins, outs):
+            fa.fa_fwd(q, k, v, o, lse, stream=stream)
+
+    work(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = [(o.clone(), lse.clone()) for o, lse in outs]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work(torch.cuda.current_stream())
+
+    for rep in range(3):
+        for o, lse in outs:
+            o.fill_(float("nan"))
+            lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, ((o, lse), (ro, rl)) in enumerate(zip(outs, ref)):
+            assert torch.equal(o.view(torch.int16), ro.view(torch.int16)), f"replay {rep}: O of shape {shapes[i]}"
+            assert torch.equal(lse.view(torch.int32), rl.view(torch.int32)), f"replay {rep}: LSE of shape {shapes[i]}"
