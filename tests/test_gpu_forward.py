@@ -114,20 +114,21 @@ def test_large_magnitude_scores(gpu_lib, dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_large_magnitude_scores_eight_wave_plans(gpu_lib, dtype, d):
-    # Scores of several hundred on the 8-wave plans (at d = 64 the ping-pong schedule): the
-    # running maximum jumps on later tiles too, so tiles are redone with their own maximum
-    # while the other wave group of the SIMD runs half a tile apart.
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_magnitude_scores_eight_wave_plans(gpu_lib, dtype, d, causal):
+    # Scores of several hundred on the long-sequence plans (8 waves; at d = 64 non-causal the
+    # ping-pong schedule; causal d = 128 the 32-key plan): the running maximum jumps on later
+    # tiles too, so tiles are redone with their own maximum, next to the diagonal masks.
     import torch
 
     B, H, N = 4, 16, 2100
-    plan = gpu_lib.fa_fwd_plan(B, H, N, d, wl_dtype_code(dtype))
-    assert plan["waves"] == 8
+    plan = gpu_lib.fa_fwd_plan(B, H, N, d, wl_dtype_code(dtype), causal=causal)
+    assert plan["waves"] == (4 if causal and d == 128 else 8)
     sigma = 10.0 if dtype == "bf16" else 4.0
     q, k, _ = _random_qkv(B, H, N, d, dtype, seed=77 + d, sigma=sigma)
     v = wl.random_tensor((B, H, N, d), dtype, [77 + d, 9])
     tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
-    o, lse = gpu_lib.fa_fwd(tq, tk, tv)
+    o, lse = gpu_lib.fa_fwd(tq, tk, tv, causal=causal)
     torch.cuda.synchronize()
     rng = np.random.default_rng([77, d])
     for b in range(B):
@@ -136,8 +137,8 @@ def test_large_magnitude_scores_eight_wave_plans(gpu_lib, dtype, d):
             rr = torch.from_numpy(rows).cuda()
             Og = to_host(o[b, h].index_select(0, rr))
             Lg = lse[b, h].index_select(0, rr).cpu().numpy().astype(np.float64)
-            O_ref, L_ref = attention_rows(q[b, h], k[b, h], v[b, h], scale_of(d), rows)
-            compare(Og, Lg, O_ref, L_ref, dtype, f"x{sigma} {dtype} d{d} b{b} h{h}")
+            O_ref, L_ref = attention_rows(q[b, h], k[b, h], v[b, h], scale_of(d), rows, causal=causal)
+            compare(Og, Lg, O_ref, L_ref, dtype, f"x{sigma} {dtype} d{d} causal={causal} b{b} h{h}")
     assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
 
 
