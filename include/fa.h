@@ -35,7 +35,9 @@
  *     (B*H*N == 0) returns FA_OK and queues nothing (its pointers may be NULL);
  *     then null pointers, alignment, scale, and finally the device.
  *   - Thread safety: calls may be made concurrently from several host threads;
- *     the only global state is a read-only per-device property cache.
+ *     the only global state is a read-only per-device property cache and the
+ *     static scratch buffer of fa_fwd_splitkv_qk_noalloc (whose own calls must not
+ *     overlap on one GPU).
  */
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H
@@ -63,8 +65,12 @@ typedef enum {
     FA_ERR_SCALE = 5,       /* scale is not finite or not > 0                        */
     FA_ERR_DEVICE = 6,      /* no HIP device, or the current device is not gfx950    */
     FA_ERR_LAUNCH = 7,      /* the kernel launch was rejected by the runtime          */
-    FA_ERR_WORKSPACE = 8    /* workspace missing or smaller than required             */
+    FA_ERR_WORKSPACE = 8,   /* workspace missing or smaller than required             */
+    FA_ERR_SCRATCH = 9      /* the call needs more than the library's static scratch  */
 } fa_status;
+
+/* Bytes of the per-device static scratch buffer behind fa_fwd_splitkv_qk_noalloc. */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* Launch plan the tile/occupancy chooser picks for a forward problem. */
 typedef struct {
@@ -145,6 +151,25 @@ fa_status fa_fwd_splitkv_qk(const void* Q, const void* K, const void* V, void* O
                             void* workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
                             int64_t Nk, int64_t d, float scale, fa_dtype dtype, int32_t splits,
                             void* stream);
+
+/*
+ * fa_fwd_splitkv_qk without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The split partials go to a static device buffer of
+ * FA_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it runs on until
+ * the process ends; its address is looked up once per device, on the first call there.
+ * Same arguments (minus workspace / ws_bytes), layouts, results and errors as
+ * fa_fwd_splitkv_qk; a call whose split partials need more than the static buffer
+ * (fa_fwd_splitkv_qk_workspace_bytes(...) > FA_NOALLOC_SCRATCH_BYTES) returns
+ * FA_ERR_SCRATCH before queuing anything.  Every call on one GPU shares that GPU's
+ * buffer: calls that can overlap on one GPU (different streams, or host threads without
+ * ordering) race on it and must be serialised by the caller.  Calls on one stream are
+ * ordered and safe.  With one split (the chooser's answer for full grids) no scratch is
+ * used at all.
+ */
+fa_status fa_fwd_splitkv_qk_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                    fa_dtype dtype, int32_t splits, void* stream);
 
 /*
  * Workspace the backward needs, in bytes: two fp32 values per row (B*H*N rows).

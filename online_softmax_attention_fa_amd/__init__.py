@@ -20,13 +20,16 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_ALIGN",
-    5: "FA_ERR_SCALE", 6: "FA_ERR_DEVICE", 7: "FA_ERR_LAUNCH", 8: "FA_ERR_WORKSPACE",
+    5: "FA_ERR_SCALE", 6: "FA_ERR_DEVICE", 7: "FA_ERR_LAUNCH", 8: "FA_ERR_WORKSPACE", 9: "FA_ERR_SCRATCH",
 }
+
+# Bytes of the static device scratch behind fa_fwd_splitkv_qk_noalloc (FA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_causal", "fa_fwd_plan", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_splits",
            "fa_fwd_splitkv", "fa_fwd_splitkv_qk_workspace_bytes", "fa_fwd_splitkv_qk_splits", "fa_fwd_splitkv_qk",
-           "fa_fp8_padded_len", "fa_fp8_scale_blocks", "fa_quantize_fp8", "fa_fwd_fp8",
+           "fa_fwd_splitkv_qk_noalloc", "fa_fp8_padded_len", "fa_fp8_scale_blocks", "fa_quantize_fp8", "fa_fwd_fp8",
            "fa_fwd_fp8_causal",           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal", "fa_status_str", "fa_version")
 
 
@@ -79,6 +82,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_splitkv_qk.argtypes = [P, P, P, P, P, P, ctypes.c_size_t, I64, I64, I64, I64, I64, F, I,
                                       ctypes.c_int32, P]
     lib.fa_fwd_splitkv_qk.restype = I
+    lib.fa_fwd_splitkv_qk_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I, ctypes.c_int32, P]
+    lib.fa_fwd_splitkv_qk_noalloc.restype = I
     lib.fa_fp8_padded_len.argtypes = [I64]
     lib.fa_fp8_padded_len.restype = I64
     lib.fa_fp8_scale_blocks.argtypes = [I64]
@@ -336,6 +341,39 @@ def _splitkv_qk(lib, q, k, v, o, lse, splits, workspace, scale, stream):
                                    workspace.data_ptr(), workspace.numel(), B, H, Nq, Nk, d, float(scale), code,
                                    int(splits), _stream_handle(stream))
     _check(st, "fa_fwd_splitkv_qk")
+    return o, lse
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o=None, lse=None, splits=0, scale=None, stream=None):
+    """``fa_fwd_splitkv_qk_noalloc``: the split-KV forward with its partials in the library's
+    static device scratch (no workspace argument, no allocation inside the call).  q
+    [B, H, Nq, d]; k, v [B, H, Nk, d].  o and lse are allocated here only when not given;
+    pass them for an allocation-free call.  Returns (o, lse)."""
+    import torch
+
+    lib = load()
+    if q.dim() != 4 or k.dim() != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"k must be [B, H, Nk, d] with q's B, H, d: q {tuple(q.shape)} k {tuple(k.shape)}")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous device tensor of q's dtype")
+    if v.shape != k.shape:
+        raise ValueError("v must have k's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or not o.is_cuda:
+        raise ValueError("o must be a contiguous device tensor shaped and typed like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, Nq]")
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_splitkv_qk_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                           B, H, Nq, Nk, d, float(scale), dtype_code(q.dtype), int(splits),
+                                           _stream_handle(stream))
+    _check(st, "fa_fwd_splitkv_qk_noalloc")
     return o, lse
 
 

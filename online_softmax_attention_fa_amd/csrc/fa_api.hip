@@ -12,15 +12,25 @@
 #include "fa_internal.h"
 #include "fa_splitkv.h"
 
+// Static split-KV scratch of fa_fwd_splitkv_qk_noalloc: every GPU the library runs on holds
+// its own copy for the life of the process.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels get the device address that hipGetSymbolAddress
+// returns for the current device (device_scratch below), never `scratch` itself.
+static constexpr size_t kScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 400;  // 0.4.0
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxGrid = int64_t(1) << 31;   // workgroups per launch (32-bit ids)
 
 struct DeviceInfo {
     std::once_flag once;
     bool gfx950 = false;
+    // address of this device's copy of `scratch` (fa_fwd_splitkv_qk_noalloc), looked up once
+    std::once_flag scratch_once;
+    void* scratch = nullptr;
 };
 DeviceInfo g_devices[kMaxDevices];
 
@@ -39,6 +49,23 @@ fa_status check_device() {
         (void)hipGetLastError();
     });
     return info.gfx950 ? FA_OK : FA_ERR_DEVICE;
+}
+
+// Device address of the current device's `scratch` (the device must have passed
+// check_device), or nullptr if the runtime could not resolve it.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    DeviceInfo& info = g_devices[dev];
+    std::call_once(info.scratch_once, [&] {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) info.scratch = ptr;
+        else (void)hipGetLastError();
+    });
+    return info.scratch;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -113,9 +140,11 @@ int32_t effective_splits(int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d,
     return splits > tiles ? (int32_t)tiles : splits;
 }
 
+// use_scratch: the partials go to the static `scratch` (fa_fwd_splitkv_qk_noalloc); ws and
+// ws_bytes are then ignored.
 fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, float* LSE, void* ws,
                          size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d, float scale,
-                         fa_dtype dtype, int32_t splits, void* stream) {
+                         fa_dtype dtype, int32_t splits, void* stream, bool use_scratch = false) {
     fa_status st = check_splitkv(B, H, N, Nk, d, dtype, splits);
     if (st != FA_OK) return st;
     if (B * H * N == 0) return FA_OK;
@@ -128,9 +157,17 @@ fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, f
     if (splits <= 1) return fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, dtype, stream, 0, Nk);
     if (B * H * fa::ceil_div(N, 128) * splits >= kMaxGrid) return FA_ERR_SHAPE;
     const size_t need = fa::splitkv_workspace_bytes(B, H, N, d, splits);
-    if (!ws || !aligned(ws, 256) || ws_bytes < need) return FA_ERR_WORKSPACE;
+    if (use_scratch) {
+        if (need > kScratchBytes) return FA_ERR_SCRATCH;
+    } else if (!ws || !aligned(ws, 256) || ws_bytes < need) {
+        return FA_ERR_WORKSPACE;
+    }
     st = check_device();
     if (st != FA_OK) return st;
+    if (use_scratch) {
+        ws = device_scratch();
+        if (!ws) return FA_ERR_DEVICE;
+    }
 
     fa::FwdArgs a;
     a.q = Q;
@@ -219,6 +256,13 @@ fa_status fa_fwd_splitkv_qk(const void* Q, const void* K, const void* V, void* O
                             size_t ws_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                             fa_dtype dtype, int32_t splits, void* stream) {
     return splitkv_common(Q, K, V, O, LSE, workspace, ws_bytes, B, H, Nq, Nk, d, scale, dtype, splits, stream);
+}
+
+fa_status fa_fwd_splitkv_qk_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
+                                    int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, fa_dtype dtype,
+                                    int32_t splits, void* stream) {
+    return splitkv_common(Q, K, V, O, LSE, nullptr, 0, B, H, Nq, Nk, d, scale, dtype, splits, stream,
+                          /*use_scratch=*/true);
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype, int32_t splits) {
@@ -362,6 +406,8 @@ const char* fa_status_str(fa_status s) {
         case FA_ERR_DEVICE: return "FA_ERR_DEVICE: no HIP device or the current device is not gfx950";
         case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+        case FA_ERR_SCRATCH:
+            return "FA_ERR_SCRATCH: the split partials need more than the static scratch (FA_NOALLOC_SCRATCH_BYTES)";
     }
     return "FA_ERR_UNKNOWN";
 }

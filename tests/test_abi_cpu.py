@@ -372,3 +372,45 @@ def test_heads_beyond_32_bit_byte_offsets_are_shape_errors(lib):
     assert lib.fa_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1 << 23, 128, 0.125, fa.FA_BF16, None) == 2
     plan = fa.Plan()
     assert lib.fa_fwd_plan(1, 1, (1 << 23) - 1, 128, fa.FA_BF16, 0, ctypes.byref(plan)) == 0
+
+
+def _noalloc(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, H=4, Nq=1, Nk=5000, d=128, scale=0.125,
+             dtype=fa.FA_BF16, splits=0):
+    return lib.fa_fwd_splitkv_qk_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits, None)
+
+
+def test_noalloc_validates_like_splitkv_qk(lib):
+    assert lib.fa_status_str(9).decode().startswith("FA_ERR_SCRATCH")
+    assert _noalloc(lib, Nk=0) == 2
+    assert _noalloc(lib, Nq=-1) == 2
+    assert _noalloc(lib, splits=65) == 2
+    assert _noalloc(lib, d=96) == 3
+    assert _noalloc(lib, dtype=fa.FA_F32) == 3
+    assert _noalloc(lib, Nq=0, Nk=0, q=None) == 0
+    assert _noalloc(lib, v=None) == 1
+    assert _noalloc(lib, o=FAKE + 8) == 4
+    assert _noalloc(lib, lse=FAKE + 2) == 4
+    assert _noalloc(lib, scale=float("nan")) == 5
+
+
+def test_noalloc_rejects_partials_beyond_the_static_scratch(lib):
+    limit = fa.NOALLOC_SCRATCH_BYTES
+    assert limit == 32 << 20
+    # 8 splits of 8192 rows x 128 dims of fp32 partials: 32 MiB + the LSE partials > limit
+    B, H, Nq, Nk, d, s = 1, 8, 1024, 8192, 128, 8
+    need = lib.fa_fwd_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, fa.FA_BF16, s)
+    assert need > limit
+    assert _noalloc(lib, B=B, H=H, Nq=Nq, Nk=Nk, d=d, splits=s) == 9
+    # the same rows in 7 splits fit
+    assert lib.fa_fwd_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, fa.FA_BF16, 7) <= limit
+    # the size check precedes the device check, so it holds without a GPU as well
+
+
+def test_noalloc_valid_calls_without_gpu_stop_at_device_check(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; the device check passes")
+    assert _noalloc(lib) == 6                       # decode shape, several splits
+    assert _noalloc(lib, B=1, H=8, Nq=1024, Nk=8192, splits=7) == 6
+    assert _noalloc(lib, splits=1) == 6             # one split: the plain forward, no scratch
