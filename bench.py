@@ -26,6 +26,13 @@ ONE JSON line on stdout (everything else goes to stderr):
   power      socket power and GFX clock (amd-smi) sampled while the forward runs back to back
              for --power-seconds after the timed steps, with the board's power cap; the
              kernel is power-bound on this workload, so these numbers bound its rate
+  configs    forward time of the four other workloads at their real sizes: fp32 B1 H1 N256
+             d64 (latency-bound), bf16 B4 H16 N2048 d64, fp16 B1 H32 N16384 d128 and the edge
+             workload bf16 B2 H8 N4097 d128 (zero, x10 and one-hot heads); median and min of
+             per-launch events, TFLOP/s and % of the MFMA peak of the input type
+  hbm_small_n  short sequences at B*H = 1024, d = 128, bf16, N in {128, 256, 512}, where the
+             forward is bounded by HBM: algorithmic bytes (Q, K, V read once, O and LSE
+             written once) per launch time, as GB/s and % of the 8 TB/s HBM peak
   sweep      (--sweep only) forward time of the smaller workloads (fp32 B1 H1 N256 d64,
              bf16 B4 H16 N2048 d64, fp16 B1 H32 N16384 d128, bf16 B2 H8 N4097 d128), the
              causal and split-KV variants, the fp8 forward causal at d=128 and at d=64,
@@ -44,12 +51,16 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) and % of MI355X bf16 MFMA peak, d=128"
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_FP8_TFLOPS = 5033.2           # MI355X dense fp8 MFMA: 256 CU x 8192 FLOP/clk x 2.4 GHz
+PEAK_FP32_TFLOPS = 157.3           # MI355X fp32 (vector and matrix)
+PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 B, H, N, D = 4, 32, 16384, 128
 KERNEL_SOURCES = ("online_softmax_attention_fa_amd/csrc/fa_fwd_kernel.hip",
                   "online_softmax_attention_fa_amd/csrc/fa_device.h",
@@ -143,6 +154,50 @@ def cpu_baseline(q, k, v, o, lse, scale, budget_s=15.0, chunk=2048):
     }
 
 
+def backward_sample_check(q, k, v, do, dq, dk, dv, scale, heads=1, nrows=64, ncols=32):
+    """The oracle's gradients on sampled rows (dQ) and columns (dK, dV) of ``heads`` seeded
+    heads of the workload, against the GPU's: bare max-abs error per gradient, and the count
+    of elements above 1e-2 + half a bf16 ulp of the reference (the rule that holds O's
+    tolerance up to the rounding of the stored output)."""
+    import numpy as np
+
+    from oracle import backward_cols_dkdv, backward_rows_dq
+
+    rng = np.random.default_rng(20240603)
+    out = {"heads": [], "rows_per_head": nrows, "cols_per_head": ncols}
+    worst = {"dq": [0.0, 0, 0.0], "dk": [0.0, 0, 0.0], "dv": [0.0, 0, 0.0]}   # max err, count over, max |ref|
+    t0 = time.perf_counter()
+
+    def half_ulp_bf16(x):
+        ax = np.abs(x)
+        e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+        return 0.5 * np.exp2(np.maximum(e, -126) - 7)
+
+    def upd(key, got, ref):
+        err = np.abs(got - ref)
+        w = worst[key]
+        w[0] = max(w[0], float(err.max()))
+        w[1] += int((err > 1e-2 + half_ulp_bf16(ref)).sum())
+        w[2] = max(w[2], float(np.abs(ref).max()))
+
+    for bh in rng.choice(B * H, size=heads, replace=False):
+        b, hh = divmod(int(bh), H)
+        f64 = lambda t: t[b, hh].float().cpu().numpy().astype(np.float64)
+        Q, K, V, dO = f64(q), f64(k), f64(v), f64(do)
+        rows = np.unique(np.concatenate([[0, 127, 128, N - 1], rng.choice(N, nrows - 4, replace=False)]))
+        cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, ncols - 2, replace=False)]))
+        upd("dq", f64(dq)[rows], backward_rows_dq(Q, K, V, dO, scale, rows))
+        dk_ref, dv_ref = backward_cols_dkdv(Q, K, V, dO, scale, cols)
+        upd("dk", f64(dk)[cols], dk_ref)
+        upd("dv", f64(dv)[cols], dv_ref)
+        out["heads"].append([b, hh])
+    for key, (e, n, r) in worst.items():
+        out[key] = {"max_abs_err": e, "n_above_1e-2_plus_half_ulp": n, "max_abs_ref": r}
+    out["seconds"] = round(time.perf_counter() - t0, 2)
+    log(f"backward sample check: {out}")
+    return out
+
+
 def time_backward(fa, q, k, v, o, lse, scale, stream, steps):
     """fa_bwd on the forward's O and LSE with seeded dO; events on the launch stream."""
     import torch
@@ -167,7 +222,7 @@ def time_backward(fa, q, k, v, o, lse, scale, stream, steps):
     log(f"backward {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (10*B*H*N^2*d), finite={ok}")
     return {"ms_per_step": round(ms, 4), "tflops": round(tflops, 2), "steps": steps,
             "flops_per_step": flops, "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-            "outputs_finite": ok}
+            "outputs_finite": ok}, (do, dq, dk, dv)
 
 
 def time_fp8(fa, q, k, v, o_ref, scale, stream, steps):
@@ -280,6 +335,94 @@ def launch_times(fn, stream, steps, warmup=5):
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
 
+def _timed_case(fa, stream, q, k, v, scale, steps):
+    import statistics
+
+    import torch
+
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], device=q.device, dtype=torch.float32)
+    t = launch_times(lambda: fa.fa_fwd(q, k, v, o, lse, scale=scale, stream=stream), stream, steps)
+    ok = bool(torch.isfinite(o).all().item() and torch.isfinite(lse).all().item())
+    return min(t), statistics.median(t), ok
+
+
+def _upload(x, dtype, dev):
+    """Exactly representable float64 values -> device tensor of the storage dtype."""
+    import torch
+
+    import workloads as wl
+
+    arr = wl.storage_array(x, dtype)
+    if dtype == "bf16":
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(arr).to(dev)
+
+
+def configs_leg(fa, stream, steps=20):
+    """The forward at the other workloads' real sizes.  fp32 B1 H1 N256 d64 and the edge
+    workload bf16 B2 H8 N4097 d128 take the seeded inputs of the workloads module (the edge
+    one with its zero, x10 and one-hot heads); the two larger iid ones draw N(0,1) on the
+    device (torch Philox), the same distribution without 200M host draws."""
+    import torch
+
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(20240604)
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+    rows = []
+    for cid in (1, 2, 3, 4):
+        w = wl.WORKLOADS[cid]
+        dt = tdt[w.dtype]
+        if cid in (1, 4):
+            q, k, v = (_upload(x, w.dtype, dev) for x in wl.make_inputs(w, threads=8))
+            source = "workloads module (seeded numpy)"
+        else:
+            q, k, v = (torch.randn(w.B, w.H, w.N, w.d, device=dev, dtype=dt, generator=gen) for _ in range(3))
+            source = "device N(0,1), torch Philox"
+        tmin, tmed, ok = _timed_case(fa, stream, q, k, v, w.scale, steps)
+        peak = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
+        tf = w.flops / (tmed * 1e-3) / 1e12
+        nbytes = 4.0 * w.B * w.H * w.N * w.d * q.element_size() + 4.0 * w.B * w.H * w.N
+        r = {"workload": f"{w.dtype} B{w.B} H{w.H} N{w.N} d{w.d}" + (" edge heads" if w.kind == "edge" else ""),
+             "median_us": round(1e3 * tmed, 2), "min_us": round(1e3 * tmin, 2), "tflops": round(tf, 2),
+             "pct_of_mfma_peak": round(100 * tf / peak, 2), "peak_tflops": peak,
+             "gbps_algorithmic": round(nbytes / (tmed * 1e-3) / 1e9, 1),
+             "plan": fa.fa_fwd_plan(w.B, w.H, w.N, w.d, dt), "outputs_finite": ok, "inputs": source}
+        if cid == 1:
+            r["note"] = "latency-bound (8 workgroups): microseconds and GB/s, no roofline claim"
+        rows.append(r)
+        log(f"config {r['workload']}: median {r['median_us']} us, {r['tflops']} TFLOP/s = "
+            f"{r['pct_of_mfma_peak']}% of peak, finite={ok}")
+        del q, k, v
+    return rows
+
+
+def hbm_small_n_leg(fa, stream, steps=20):
+    """Short sequences at B*H = 1024, d = 128, bf16: algorithmic bytes over launch time."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(20240605)
+    b, h, d = 16, 64, 128
+    rows = []
+    for n in (128, 256, 512):
+        q, k, v = (torch.randn(b, h, n, d, device=dev, dtype=torch.bfloat16, generator=gen) for _ in range(3))
+        tmin, tmed, ok = _timed_case(fa, stream, q, k, v, 1.0 / math.sqrt(d), steps)
+        nbytes = 4.0 * b * h * n * d * 2 + 4.0 * b * h * n
+        gbps = nbytes / (tmed * 1e-3) / 1e9
+        rows.append({"workload": f"bf16 B{b} H{h} N{n} d{d}", "median_us": round(1e3 * tmed, 2),
+                     "min_us": round(1e3 * tmin, 2), "algorithmic_bytes": nbytes, "gbps": round(gbps, 1),
+                     "pct_of_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+                     "flop_per_byte": round(4.0 * b * h * n * n * d / nbytes, 1),
+                     "plan": fa.fa_fwd_plan(b, h, n, d, torch.bfloat16), "outputs_finite": ok})
+        log(f"hbm small N={n}: median {rows[-1]['median_us']} us, {rows[-1]['gbps']} GB/s = "
+            f"{rows[-1]['pct_of_hbm_peak']}% of 8 TB/s")
+        del q, k, v
+    return rows
+
+
 def sweep(fa, stream, steps=20):
     """Forward timings of the smaller workloads, the bandwidth-bound short sequences, a decode
     shape, and one small call replayed from a captured graph."""
@@ -371,6 +514,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--sweep", action="store_true", help="also time the smaller workloads")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' forward timings")
+    ap.add_argument("--no-hbm-small-n", action="store_true", help="skip the short-sequence HBM leg")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--fp8-steps", type=int, default=10)
     ap.add_argument("--power-seconds", type=float, default=4.0,
@@ -476,14 +621,21 @@ def main():
                 achieved / (PEAK_BF16_TFLOPS * pw["gfx_mhz_mean"] / 2400.0), 4)
         out["power"] = pw
         log(f"power: {pw}")
+    grads = None
     if not args.no_backward:
-        out["backward"] = time_backward(fa, q, k, v, o, lse, scale, stream, args.backward_steps)
+        out["backward"], grads = time_backward(fa, q, k, v, o, lse, scale, stream, args.backward_steps)
     if not args.no_fp8:
         out["fp8"] = time_fp8(fa, q, k, v, o, scale, stream, args.fp8_steps)
+    if not args.no_configs:
+        out["configs"] = configs_leg(fa, stream)
+    if not args.no_hbm_small_n:
+        out["hbm_small_n"] = hbm_small_n_leg(fa, stream)
     if args.sweep:
         out["sweep"] = sweep(fa, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, o, lse, scale)
+        if grads is not None:
+            out["cpu_baseline"]["backward_sample_check"] = backward_sample_check(q, k, v, *grads, scale)
     print(json.dumps(out), flush=True)
 
 

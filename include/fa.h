@@ -34,6 +34,18 @@
  *   - Validation order: shapes, head dim / dtype; then an empty problem
  *     (B*H*N == 0) returns FA_OK and queues nothing (its pointers may be NULL);
  *     then null pointers, alignment, scale, and finally the device.
+ *   - Environment (read on every call, host only):
+ *       FA_TILE=Br,Bc,W  replaces the tile chooser's plan for fa_fwd, fa_fwd_causal and
+ *                        fa_fwd_plan (and split-KV calls that run as one split) with Br
+ *                        query rows per workgroup, Bc keys per K/V tile and W waves, for
+ *                        measuring tile choices ("从零理解Flash Attention中的online softmax",
+ *                        section 6.1, picks tiles by measurement per GPU).  It must name a
+ *                        compiled kernel for the call's dtype and head dim -- bf16/fp16:
+ *                        d = 128: 256,128,8  128,64,4  128,32,4;  d = 64: 256,128,8
+ *                        128,128,4  128,64,4;  fp32: 32,32,4 -- else those calls return
+ *                        FA_ERR_TILE.  Unset or empty: the chooser decides.
+ *       FA_LOG=1         prints each call's plan (tiles, waves, grid, LDS, splits) to
+ *                        stderr as soon as it is chosen, before the device check.
  *   - Thread safety: calls may be made concurrently from several host threads;
  *     the only global state is a read-only per-device property cache and the
  *     static scratch buffer of fa_fwd_splitkv_qk_noalloc (whose own calls must not
@@ -66,7 +78,8 @@ typedef enum {
     FA_ERR_DEVICE = 6,      /* no HIP device, or the current device is not gfx950    */
     FA_ERR_LAUNCH = 7,      /* the kernel launch was rejected by the runtime          */
     FA_ERR_WORKSPACE = 8,   /* workspace missing or smaller than required             */
-    FA_ERR_SCRATCH = 9      /* the call needs more than the library's static scratch  */
+    FA_ERR_SCRATCH = 9,     /* the call needs more than the library's static scratch  */
+    FA_ERR_TILE = 10        /* FA_TILE names no compiled kernel for this problem      */
 } fa_status;
 
 /* Bytes of the per-device static scratch buffer behind fa_fwd_splitkv_qk_noalloc. */

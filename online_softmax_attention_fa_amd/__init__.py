@@ -21,6 +21,7 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_ALIGN",
     5: "FA_ERR_SCALE", 6: "FA_ERR_DEVICE", 7: "FA_ERR_LAUNCH", 8: "FA_ERR_WORKSPACE", 9: "FA_ERR_SCRATCH",
+    10: "FA_ERR_TILE",
 }
 
 # Bytes of the static device scratch behind fa_fwd_splitkv_qk_noalloc (FA_NOALLOC_SCRATCH_BYTES).
@@ -30,7 +31,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 EXPORTS = ("fa_fwd", "fa_fwd_causal", "fa_fwd_plan", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv_splits",
            "fa_fwd_splitkv", "fa_fwd_splitkv_qk_workspace_bytes", "fa_fwd_splitkv_qk_splits", "fa_fwd_splitkv_qk",
            "fa_fwd_splitkv_qk_noalloc", "fa_fp8_padded_len", "fa_fp8_scale_blocks", "fa_quantize_fp8", "fa_fwd_fp8",
-           "fa_fwd_fp8_causal",           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal", "fa_status_str", "fa_version")
+           "fa_fwd_fp8_causal", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_causal", "fa_status_str", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -136,6 +137,37 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_device(t, name, device):
+    """Every pointer handed to the library must be device memory on the call's GPU: a host
+    pointer would reach the kernels as an unmapped address."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device} (got {t.device})")
+
+
+def _check_tensor(t, name, device, shape, dtype):
+    """Caller-supplied buffer: shape, dtype, contiguity and device, before any C call."""
+    _on_device(t, name, device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous {dtype} {tuple(shape)}; got {t.dtype} {tuple(t.shape)}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _workspace(workspace, need, device):
+    """The caller's workspace (any dtype, contiguous, on the call's device), or a new one."""
+    import torch
+
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _on_device(workspace, "workspace", device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _check_qkv(q, k, v):
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
@@ -144,6 +176,7 @@ def _check_qkv(q, k, v):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
+        _on_device(t, name, q.device)
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         if t.dtype != q.dtype:
@@ -168,10 +201,8 @@ def fa_fwd(q, k, v, o=None, lse=None, scale=None, stream=None, causal=False):
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
-        raise ValueError("o must be contiguous, shaped and typed like q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    _check_tensor(o, "o", q.device, q.shape, q.dtype)
+    _check_tensor(lse, "lse", q.device, (B, H, N), torch.float32)
     fn = lib.fa_fwd_causal if causal else lib.fa_fwd
     with torch.cuda.device(q.device):
         st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -215,7 +246,7 @@ def fa_fwd_splitkv(q, k, v, o=None, lse=None, splits=0, workspace=None, scale=No
     import torch
 
     lib = load()
-    if k.dim() != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+    if q.dim() != 4 or k.dim() != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
         raise ValueError(f"k must be [B, H, Nk, d] with q's B, H, d: q {tuple(q.shape)} k {tuple(k.shape)}")
     if k.shape[2] != q.shape[2]:
         return _splitkv_qk(lib, q, k, v, o, lse, splits, workspace, scale, stream)
@@ -225,17 +256,14 @@ def fa_fwd_splitkv(q, k, v, o=None, lse=None, splits=0, workspace=None, scale=No
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
-        raise ValueError("o must be contiguous, shaped and typed like q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    _check_tensor(o, "o", q.device, q.shape, q.dtype)
+    _check_tensor(lse, "lse", q.device, (B, H, N), torch.float32)
     code = dtype_code(q.dtype)
     need = int(lib.fa_fwd_splitkv_workspace_bytes(B, H, N, d, code, splits))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     with torch.cuda.device(q.device):
         st = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                workspace.data_ptr(), workspace.numel(), B, H, N, d, float(scale), code,
+                                workspace.data_ptr(), _nbytes(workspace), B, H, N, d, float(scale), code,
                                 int(splits), _stream_handle(stream))
     _check(st, "fa_fwd_splitkv")
     return o, lse
@@ -265,10 +293,8 @@ def fa_quantize_fp8(x, transpose=False, x8=None, scales=None, stream=None):
     shape = (B, H, d, fa_fp8_padded_len(N)) if transpose else (B, H, N, d)
     x8 = torch.empty(shape, dtype=torch.uint8, device=x.device) if x8 is None else x8
     scales = torch.empty((B, H, fa_fp8_scale_blocks(N)), dtype=torch.float32, device=x.device) if scales is None else scales
-    if tuple(x8.shape) != shape or x8.dtype != torch.uint8 or not x8.is_contiguous():
-        raise ValueError(f"x8 must be contiguous uint8 {shape}")
-    if tuple(scales.shape) != (B, H, fa_fp8_scale_blocks(N)) or scales.dtype != torch.float32:
-        raise ValueError("scales must be fp32 [B, H, ceil(N / 64)]")
+    _check_tensor(x8, "x8", x.device, shape, torch.uint8)
+    _check_tensor(scales, "scales", x.device, (B, H, fa_fp8_scale_blocks(N)), torch.float32)
     with torch.cuda.device(x.device):
         st = lib.fa_quantize_fp8(x.data_ptr(), x8.data_ptr(), scales.data_ptr(), B, H, N, d,
                                  dtype_code(x.dtype), 1 if transpose else 0, _stream_handle(stream))
@@ -292,20 +318,19 @@ def fa_fwd_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, o=None, lse=None, scale=N
     nb = fa_fp8_scale_blocks(N)
     if k8.shape != q8.shape or tuple(vt8.shape) != (B, H, d, fa_fp8_padded_len(N)):
         raise ValueError("k8 must match q8; vt8 must be [B, H, d, Np]")
-    for t in (q8, k8, vt8):
-        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("codes must be contiguous uint8 device tensors")
-    for t in (q_scale, k_scale, v_scale):
-        if tuple(t.shape) != (B, H, nb) or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("scales must be contiguous fp32 [B, H, ceil(N / 64)]")
+    if not q8.is_cuda:
+        raise ValueError("codes must be contiguous uint8 device tensors")
+    dev = q8.device
+    for arg, t in (("q8", q8), ("k8", k8), ("vt8", vt8)):
+        _check_tensor(t, arg, dev, t.shape, torch.uint8)
+    for arg, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_tensor(t, arg, dev, (B, H, nb), torch.float32)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty((B, H, N, d), dtype=out_dtype, device=q8.device) if o is None else o
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
-    if tuple(o.shape) != (B, H, N, d) or o.dtype != out_dtype or not o.is_contiguous():
-        raise ValueError("o must be contiguous [B, H, N, d] of out_dtype")
-    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=dev) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check_tensor(o, "o", dev, (B, H, N, d), out_dtype)
+    _check_tensor(lse, "lse", dev, (B, H, N), torch.float32)
     with torch.cuda.device(q8.device):
         st = getattr(lib, name)(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_scale.data_ptr(),
                                 k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
@@ -319,28 +344,38 @@ def _splitkv_qk(lib, q, k, v, o, lse, splits, workspace, scale, stream):
 
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
+    o, lse = _qk_common(q, k, v, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = dtype_code(q.dtype)
+    need = int(lib.fa_fwd_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, code, splits))
+    workspace = _workspace(workspace, need, q.device)
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_splitkv_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   workspace.data_ptr(), _nbytes(workspace), B, H, Nq, Nk, d, float(scale), code,
+                                   int(splits), _stream_handle(stream))
+    _check(st, "fa_fwd_splitkv_qk")
+    return o, lse
+
+
+def _qk_common(q, k, v, o, lse):
+    """Checks of a call with Nq query rows and Nk keys per head; returns (o, lse), allocated
+    when not given."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"k must be [B, H, Nk, d] with q's B, H, d: q {tuple(q.shape)} k {tuple(k.shape)}")
+    B, H, Nq, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
             raise ValueError(f"{name} must be a contiguous device tensor of q's dtype")
+        _on_device(t, name, q.device)
     if v.shape != k.shape:
         raise ValueError("v must have k's shape")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous():
-        raise ValueError("o must be contiguous, shaped and typed like q")
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B, H, Nq]")
-    code = dtype_code(q.dtype)
-    need = int(lib.fa_fwd_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, code, splits))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    with torch.cuda.device(q.device):
-        st = lib.fa_fwd_splitkv_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                   workspace.data_ptr(), workspace.numel(), B, H, Nq, Nk, d, float(scale), code,
-                                   int(splits), _stream_handle(stream))
-    _check(st, "fa_fwd_splitkv_qk")
+    _check_tensor(o, "o", q.device, q.shape, q.dtype)
+    _check_tensor(lse, "lse", q.device, (B, H, Nq), torch.float32)
     return o, lse
 
 
@@ -352,23 +387,11 @@ def fa_fwd_splitkv_noalloc(q, k, v, o=None, lse=None, splits=0, scale=None, stre
     import torch
 
     lib = load()
-    if q.dim() != 4 or k.dim() != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
-        raise ValueError(f"k must be [B, H, Nk, d] with q's B, H, d: q {tuple(q.shape)} k {tuple(k.shape)}")
+    o, lse = _qk_common(q, k, v, o, lse)
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be a contiguous device tensor of q's dtype")
-    if v.shape != k.shape:
-        raise ValueError("v must have k's shape")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if o is None else o
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or not o.is_cuda:
-        raise ValueError("o must be a contiguous device tensor shaped and typed like q")
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous fp32 device tensor [B, H, Nq]")
     with torch.cuda.device(q.device):
         st = lib.fa_fwd_splitkv_qk_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                            B, H, Nq, Nk, d, float(scale), dtype_code(q.dtype), int(splits),
@@ -398,26 +421,22 @@ def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None, scale
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     for name, t in (("o", o), ("do", do)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous device tensor shaped and typed like q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+        _check_tensor(t, name, q.device, q.shape, q.dtype)
+    _check_tensor(lse, "lse", q.device, (B, H, N), torch.float32)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous, shaped and typed like q")
+        _check_tensor(t, name, q.device, q.shape, q.dtype)
     code = dtype_code(q.dtype)
     need = int(lib.fa_bwd_workspace_bytes(B, H, N, d, code))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     fn = lib.fa_bwd_causal if causal else lib.fa_bwd
     with torch.cuda.device(q.device):
         st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), _nbytes(workspace),
                 B, H, N, d, float(scale), code, _stream_handle(stream))
     _check(st, "fa_bwd_causal" if causal else "fa_bwd")
     return dq, dk, dv

@@ -6,6 +6,8 @@
 
 #include <math.h>
 #include <mutex>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "fa_fp8.h"
@@ -68,6 +70,24 @@ void* device_scratch() {
     return info.scratch;
 }
 
+// FA_LOG set (and not "0"): each launch prints its plan to stderr.  Read on every call.
+bool log_enabled() {
+    const char* e = getenv("FA_LOG");
+    return e && *e && strcmp(e, "0") != 0;
+}
+
+const char* dtype_name(int dtype) { return dtype == FA_F32 ? "fp32" : dtype == FA_F16 ? "fp16" : "bf16"; }
+
+// The chooser's plan, or the FA_TILE override when set (FA_ERR_TILE if it names no compiled
+// kernel for this dtype and head dim).  *overridden tells which.
+fa_status make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal, fa_plan* plan,
+                    bool* overridden) {
+    *plan = fa::choose_fwd_plan(B, H, N, d, dtype, causal);
+    const char* tile = getenv("FA_TILE");
+    *overridden = tile && *tile;
+    return fa::apply_tile_override(plan, tile, B, H, N, d, dtype, causal) ? FA_OK : FA_ERR_TILE;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Shape / dtype checks shared by the plan query and the launches.
@@ -96,8 +116,16 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
         return FA_ERR_ALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
-    const fa_plan plan = fa::choose_fwd_plan(B, H, N, d, dtype, causal);
+    fa_plan plan;
+    bool overridden;
+    st = make_plan(B, H, N, d, dtype, causal, &plan, &overridden);
+    if (st != FA_OK) return st;
     if (plan.grid >= kMaxGrid) return FA_ERR_SHAPE;
+    if (log_enabled())
+        fprintf(stderr, "fa_fwd%s: B=%lld H=%lld N=%lld Nk=%lld d=%lld %s -> Br=%d Bc=%d waves=%d grid=%lld lds=%d%s%s\n",
+                causal ? "_causal" : "", (long long)B, (long long)H, (long long)N, (long long)Nk, (long long)d,
+                dtype_name(dtype), plan.block_q, plan.block_k, plan.waves, (long long)plan.grid, plan.lds_bytes,
+                plan.wave_kv_splits > 1 ? " (waves split the key tiles)" : "", overridden ? " (FA_TILE)" : "");
     st = check_device();
     if (st != FA_OK) return st;
 
@@ -162,6 +190,13 @@ fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, f
     } else if (!ws || !aligned(ws, 256) || ws_bytes < need) {
         return FA_ERR_WORKSPACE;
     }
+    if (log_enabled())
+        fprintf(stderr,
+                "fa_fwd_splitkv: B=%lld H=%lld Nq=%lld Nk=%lld d=%lld %s -> splits=%d of %lld key tiles (Bc=%d), "
+                "grid=%lld, partials %zu bytes in %s\n",
+                (long long)B, (long long)H, (long long)N, (long long)Nk, (long long)d, dtype_name(dtype), splits,
+                (long long)tiles, fa::splitkv_block_k(d), (long long)(B * H * fa::ceil_div(N, 128) * splits), need,
+                use_scratch ? "the static scratch" : "the caller's workspace");
     st = check_device();
     if (st != FA_OK) return st;
     if (use_scratch) {
@@ -212,6 +247,10 @@ fa_status bwd_common(const void* Q, const void* K, const void* V, const void* O,
         return FA_ERR_ALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
     if (!ws || !aligned(ws, 256) || ws_bytes < fa::bwd_workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+    if (log_enabled())
+        fprintf(stderr, "fa_bwd%s: B=%lld H=%lld N=%lld d=%lld %s -> preprocess, dQ over 128-row query blocks, "
+                "dK/dV over 128-key blocks\n", causal ? "_causal" : "", (long long)B, (long long)H, (long long)N,
+                (long long)d, dtype_name(dtype));
     st = check_device();
     if (st != FA_OK) return st;
 
@@ -319,6 +358,10 @@ fa_status fwd_fp8_common(const void* Q8, const void* K8, const void* Vt8, const 
         !aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(LSE, 4))
         return FA_ERR_ALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+    if (log_enabled())
+        fprintf(stderr, "fa_fwd_fp8%s: B=%lld H=%lld N=%lld d=%lld -> O %s, Br=%d Bc=64 waves=4 grid=%lld\n",
+                causal ? "_causal" : "", (long long)B, (long long)H, (long long)N, (long long)d, dtype_name(out_dtype),
+                fa::kFp8BlockQ, (long long)(B * H * fa::ceil_div(N, fa::kFp8BlockQ)));
     st = check_device();
     if (st != FA_OK) return st;
     fa::Fp8Args a;
@@ -391,7 +434,11 @@ fa_status fa_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype
     if (st != FA_OK) return st;
     memset(plan, 0, sizeof(*plan));
     if (B * H * N == 0) return FA_OK;
-    *plan = fa::choose_fwd_plan(B, H, N, d, dtype, causal);
+    bool overridden;
+    fa_plan p;
+    st = make_plan(B, H, N, d, dtype, causal, &p, &overridden);
+    if (st != FA_OK) return st;
+    *plan = p;
     return plan->grid >= kMaxGrid ? FA_ERR_SHAPE : FA_OK;
 }
 
@@ -406,6 +453,7 @@ const char* fa_status_str(fa_status s) {
         case FA_ERR_DEVICE: return "FA_ERR_DEVICE: no HIP device or the current device is not gfx950";
         case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+        case FA_ERR_TILE: return "FA_ERR_TILE: FA_TILE names no compiled kernel for this dtype and head dim";
         case FA_ERR_SCRATCH:
             return "FA_ERR_SCRATCH: the split partials need more than the static scratch (FA_NOALLOC_SCRATCH_BYTES)";
     }

@@ -8,7 +8,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/fa.h"
+#include "fa.h"
 
 namespace fa {
 
@@ -74,15 +74,20 @@ constexpr int kLdsPerCu = 160 * 1024;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// LDS bytes of one forward workgroup: K tile and transposed V tile, two stages.
-inline int fwd_lds_bytes(int dtype, int d, int block_k) {
+// LDS bytes of one forward workgroup: a K tile and a V tile per stage.
+inline int fwd_lds_bytes(int dtype, int d, int block_k, int stages) {
     const int elt = dtype == FA_F32 ? 4 : 2;
     if (dtype == FA_F32) {
         // one K and one V tile per wave (4 waves), rows padded by one element
         return 4 * 2 * block_k * (d + 1) * elt;
     }
-    return 2 * (2 * block_k * d * elt);
+    return stages * (2 * block_k * d * elt);
 }
+
+// LDS stages of a bf16/fp16 plan: three for the ping-pong schedule (8 waves, non-causal
+// d = 64), whose late wave group still reads V of the previous tile while the next one is
+// copied; two otherwise.
+inline int fwd_stages(int d, int waves, int causal) { return (waves == 8 && d == 64 && !causal) ? 3 : 2; }
 
 // The chooser.  Inputs are already validated (d in {64,128}, dtype known, N > 0).
 //
@@ -142,9 +147,60 @@ inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int d
             p.block_k = 64;   // d = 64 short heads: 64-key tiles, three workgroups per CU
     }
     p.block_q = p.waves * p.rows_per_wave / p.wave_kv_splits;
-    p.lds_bytes = fwd_lds_bytes(dtype, (int)d, p.block_k);
+    p.lds_bytes = fwd_lds_bytes(dtype, (int)d, p.block_k, fwd_stages((int)d, p.waves, causal));
     p.grid = B * H * ceil_div(N, p.block_q);
     return p;
+}
+
+// Whether a (d, Bc, waves) forward kernel is compiled for this dtype (the shapes the
+// dispatch in fa_fwd_kernel.hip launches).  fp32 has one: 32-key tiles, 4 waves.
+inline bool fwd_variant_compiled(int dtype, int64_t d, int block_k, int waves) {
+    if (dtype == FA_F32) return block_k == 32 && waves == 4;
+    if (d == 128) return (block_k == 128 && waves == 8) || (block_k == 64 && waves == 4) || (block_k == 32 && waves == 4);
+    if (d == 64) return (block_k == 128 && waves == 8) || (block_k == 128 && waves == 4) || (block_k == 64 && waves == 4);
+    return false;
+}
+
+// Query rows per workgroup of a variant: 32 per wave for bf16/fp16; 32 in all for fp32,
+// whose four waves share their rows and split the key tiles.
+inline int fwd_block_q(int dtype, int waves) { return dtype == FA_F32 ? 32 : 32 * waves; }
+
+// Parses "Br,Bc,W" (three positive decimal integers, nothing else).  Returns false if
+// malformed.
+inline bool parse_tile_override(const char* s, int* br, int* bc, int* w) {
+    int v[3];
+    for (int i = 0; i < 3; ++i) {
+        if (*s < '0' || *s > '9') return false;
+        long x = 0;
+        while (*s >= '0' && *s <= '9') {
+            x = x * 10 + (*s++ - '0');
+            if (x > 1 << 20) return false;
+        }
+        v[i] = (int)x;
+        if (i < 2 && *s++ != ',') return false;
+    }
+    if (*s != 0) return false;
+    *br = v[0], *bc = v[1], *w = v[2];
+    return true;
+}
+
+// The chooser's plan with a measured-tuning override applied: tile = "Br,Bc,W" (or NULL /
+// empty for none) replaces Br, Bc and the wave count when it names a compiled variant for
+// this dtype and head dim.  Returns false (plan untouched) when it does not.
+inline bool apply_tile_override(fa_plan* p, const char* tile, int64_t B, int64_t H, int64_t N, int64_t d,
+                                int dtype, int causal) {
+    if (!tile || !*tile) return true;
+    int br, bc, w;
+    if (!parse_tile_override(tile, &br, &bc, &w)) return false;
+    if (!fwd_variant_compiled(dtype, d, bc, w) || br != fwd_block_q(dtype, w)) return false;
+    p->block_q = br;
+    p->block_k = bc;
+    p->waves = w;
+    p->rows_per_wave = 32;
+    p->wave_kv_splits = dtype == FA_F32 ? 4 : 1;
+    p->lds_bytes = fwd_lds_bytes(dtype, (int)d, bc, fwd_stages((int)d, w, causal));
+    p->grid = B * H * ceil_div(N, br);
+    return true;
 }
 
 }  // namespace fa

@@ -374,6 +374,17 @@ def test_heads_beyond_32_bit_byte_offsets_are_shape_errors(lib):
     assert lib.fa_fwd_plan(1, 1, (1 << 23) - 1, 128, fa.FA_BF16, 0, ctypes.byref(plan)) == 0
 
 
+def test_plan_reports_the_ping_pong_third_stage(lib):
+    # non-causal d = 64 on 8 waves runs the ping-pong schedule: three 32 KiB K/V stages
+    p = fa.fa_fwd_plan(4, 16, 2048, 64, fa.FA_BF16)
+    assert (p["waves"], p["block_k"], p["lds_bytes"]) == (8, 128, 3 * 2 * 128 * 64 * 2)
+    # the causal d = 64 plan on 8 waves and the d = 128 one keep two stages
+    p = fa.fa_fwd_plan(4, 16, 2048, 64, fa.FA_BF16, causal=True)
+    assert (p["waves"], p["lds_bytes"]) == (8, 2 * 2 * 128 * 64 * 2)
+    p = fa.fa_fwd_plan(4, 32, 16384, 128, fa.FA_BF16)
+    assert (p["waves"], p["lds_bytes"]) == (8, 2 * 2 * 128 * 128 * 2)
+
+
 def _noalloc(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, H=4, Nq=1, Nk=5000, d=128, scale=0.125,
              dtype=fa.FA_BF16, splits=0):
     return lib.fa_fwd_splitkv_qk_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, dtype, splits, None)
@@ -414,3 +425,71 @@ def test_noalloc_valid_calls_without_gpu_stop_at_device_check(lib):
     assert _noalloc(lib) == 6                       # decode shape, several splits
     assert _noalloc(lib, B=1, H=8, Nq=1024, Nk=8192, splits=7) == 6
     assert _noalloc(lib, splits=1) == 6             # one split: the plain forward, no scratch
+
+
+@pytest.fixture
+def tile_env(monkeypatch):
+    """Sets FA_TILE for one test (the library reads it on every call)."""
+    def set_tile(value):
+        monkeypatch.setenv("FA_TILE", value)
+    yield set_tile
+    monkeypatch.delenv("FA_TILE", raising=False)
+
+
+def test_tile_override_replaces_the_plan(lib, tile_env):
+    base = fa.fa_fwd_plan(4, 32, 16384, 128, fa.FA_BF16)
+    assert (base["block_q"], base["block_k"], base["waves"]) == (256, 128, 8)
+    tile_env("128,64,4")
+    p = fa.fa_fwd_plan(4, 32, 16384, 128, fa.FA_BF16)
+    assert (p["block_q"], p["block_k"], p["waves"], p["grid"], p["lds_bytes"]) == (128, 64, 4, 128 * 128, 65536)
+    tile_env("128,32,4")
+    assert fa.fa_fwd_plan(2, 8, 4097, 128, fa.FA_F16, causal=True)["block_k"] == 32
+    tile_env("256,128,8")     # d = 64, non-causal: the ping-pong kernel with its third stage
+    p = fa.fa_fwd_plan(1, 2, 300, 64, fa.FA_BF16)
+    assert (p["block_q"], p["waves"], p["grid"], p["lds_bytes"]) == (256, 8, 4, 3 * 2 * 128 * 64 * 2)
+    tile_env("32,32,4")
+    p = fa.fa_fwd_plan(1, 1, 256, 64, fa.FA_F32)
+    assert (p["block_q"], p["wave_kv_splits"]) == (32, 4)
+    tile_env("")              # empty: the chooser decides
+    assert fa.fa_fwd_plan(4, 32, 16384, 128, fa.FA_BF16) == base
+
+
+@pytest.mark.parametrize("tile,d,dtype", [
+    ("128,96,4", 128, fa.FA_BF16),      # no 96-key kernel
+    ("256,64,4", 128, fa.FA_BF16),      # Br must be 32 rows per wave
+    ("128,128,4", 128, fa.FA_BF16),     # 4 waves x 128 keys is compiled for d = 64 only
+    ("128,32,4", 64, fa.FA_F16),        # 32-key tiles are compiled for d = 128 only
+    ("128,64,4", 64, fa.FA_F32),        # fp32 has one variant
+    ("abc", 128, fa.FA_BF16), ("128,64", 128, fa.FA_BF16), ("128,64,4,1", 128, fa.FA_BF16),
+    ("128, 64, 4", 128, fa.FA_BF16), ("-128,64,4", 128, fa.FA_BF16), ("99999999,64,4", 128, fa.FA_BF16),
+])
+def test_tile_override_must_name_a_compiled_kernel(lib, tile_env, tile, d, dtype):
+    tile_env(tile)
+    plan = fa.Plan()
+    assert lib.fa_fwd_plan(2, 4, 1000, d, dtype, 0, ctypes.byref(plan)) == 10
+    assert _fwd(lib, B=2, H=4, N=1000, d=d, dtype=dtype) == 10      # before the device check
+    assert _fwd(lib, B=2, H=4, N=1000, d=d, dtype=dtype, causal=True) == 10
+    assert lib.fa_status_str(10).decode().startswith("FA_ERR_TILE")
+    # calls that are not planned by the chooser ignore it
+    assert _bwd(lib, d=d, dtype=fa.FA_BF16) in (0, 6)
+
+
+def test_log_prints_the_plan_to_stderr(lib, monkeypatch, capfd):
+    monkeypatch.setenv("FA_LOG", "1")
+    _fwd(lib, B=4, H=32, N=16384, d=128)
+    _skv(lib, splits=4)
+    _bwd(lib)
+    _f8(lib)
+    monkeypatch.setenv("FA_TILE", "128,64,4")
+    _fwd(lib, B=4, H=32, N=16384, d=128)
+    monkeypatch.delenv("FA_TILE")
+    monkeypatch.setenv("FA_LOG", "0")
+    _fwd(lib, B=1, H=1, N=77, d=64)
+    err = capfd.readouterr().err
+    assert "fa_fwd: B=4 H=32 N=16384 Nk=16384 d=128 bf16 -> Br=256 Bc=128 waves=8 grid=8192 lds=131072" in err
+    assert "fa_fwd_splitkv: B=1 H=1 Nq=4096 Nk=4096 d=128 bf16 -> splits=4 of 64 key tiles" in err
+    assert "the caller's workspace" in err
+    assert "fa_bwd: B=1 H=2 N=64 d=64 bf16" in err
+    assert "fa_fwd_fp8: B=1 H=2 N=100 d=128" in err
+    assert "Br=128 Bc=64 waves=4 grid=16384 lds=65536 (FA_TILE)" in err
+    assert "N=77" not in err          # FA_LOG=0: silent
