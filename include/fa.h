@@ -61,13 +61,22 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Compiled as C++, the enumerations take int as their fixed underlying type, so any int a
+ * C caller passes (an unknown dtype, an unknown status) is a valid value for the library to
+ * receive and reject; the layout is the C enum's either way. */
+#ifdef __cplusplus
+#define FA_ENUM_INT : int
+#else
+#define FA_ENUM_INT
+#endif
+
+typedef enum FA_ENUM_INT {
     FA_F32 = 0,
     FA_F16 = 1,
     FA_BF16 = 2
 } fa_dtype;
 
-typedef enum {
+typedef enum FA_ENUM_INT {
     FA_OK = 0,
     FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
     FA_ERR_SHAPE = 2,       /* B, H or N negative, or sizes overflow the index math */
@@ -231,7 +240,7 @@ fa_status fa_bwd_causal(const void* Q, const void* K, const void* V, const void*
  * 64k .. 64k+63.  V is passed transposed, V^T [B, H, d, Np] with Np = fa_fp8_padded_len(N),
  * keys contiguous; the padding keys N..Np-1 must hold code 0 (fa_quantize_fp8 writes it).
  */
-/* Np: N rounded up to the forward's key tile (128); 0 for N < 0. */
+/* Np: N rounded up to the forward's key tile (128); 0 for N < 0 or N > INT64_MAX - 128. */
 int64_t fa_fp8_padded_len(int64_t N);
 /* nb = ceil(N / 64): scale blocks per (batch, head); 0 for N < 0. */
 int64_t fa_fp8_scale_blocks(int64_t N);

@@ -14,7 +14,11 @@ import math
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfa.so")
+# FA_LIB_PATH selects another build of the same library (the sanitizer build of the CPU
+# tests); by default the one built in-tree.
+LIB_PATH = os.environ.get("FA_LIB_PATH") or os.path.join(_PKG, "libfa.so")
+# The LDS-poison debug build (see build.py), loaded by its own tests through load_variant().
+POISON_LIB_PATH = os.path.join(_PKG, "libfa_poison.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
@@ -59,6 +63,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    _lib = load_variant(path)
+    return _lib
+
+
+def load_variant(path: str) -> ctypes.CDLL:
+    """Load a build of the library at ``path`` with its argument types set (a debug build
+    beside the in-tree one); the module's functions keep using ``load()``."""
     if not os.path.exists(path):
         raise FileNotFoundError(f"{path} is not built; run __graft_entry__.build() or "
                                 f"python -m online_softmax_attention_fa_amd.build")
@@ -104,7 +115,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = I
-    _lib = lib
     return lib
 
 

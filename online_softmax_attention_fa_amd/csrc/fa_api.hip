@@ -96,7 +96,7 @@ fa_status check_problem(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
     if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     // per-head byte offsets (16-bit elements) are 32-bit signed inside the kernels
-    if (N > 0 && N * d >= (int64_t(1) << 30)) return FA_ERR_SHAPE;
+    if (N >= (int64_t(1) << 30) / d) return FA_ERR_SHAPE;   // N * d >= 2^30, without forming N * d
     if (B > 0 && H > (int64_t(1) << 31) / B) return FA_ERR_SHAPE;
     const int64_t bh = B * H;
     if (bh > 0 && N > 0 && bh * fa::ceil_div(N, 128) >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
@@ -318,7 +318,9 @@ fa_status fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, f
     return splitkv_common(Q, K, V, O, LSE, workspace, ws_bytes, B, H, N, N, d, scale, dtype, splits, stream);
 }
 
-int64_t fa_fp8_padded_len(int64_t N) { return N < 0 ? 0 : fa::fp8_padded_len(N); }
+int64_t fa_fp8_padded_len(int64_t N) {
+    return (N < 0 || N > INT64_MAX - fa::kFp8Pad) ? 0 : fa::fp8_padded_len(N);
+}
 
 int64_t fa_fp8_scale_blocks(int64_t N) { return N < 0 ? 0 : fa::fp8_scale_blocks(N); }
 

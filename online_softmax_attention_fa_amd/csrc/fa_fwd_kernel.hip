@@ -73,6 +73,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     constexpr int TILE = BC * RB;     // bytes of one K (or V) tile
     constexpr int STAGE = 2 * TILE;
     constexpr int LOADS = TILE / (NT * 16);   // direct loads per thread per tile, K or V
+    // fp16: the fp16-rounded row sum serves O and the LSE alike (its relative error, at most
+    // 2^-11 per term, moves the LSE by less than 1e-3); bf16 keeps an fp32 sum for the LSE
+    constexpr bool ONE_SUM = __is_same(T, _Float16);
     static_assert(LOADS >= 1 && TILE % (NT * 16) == 0, "tile must be whole 4 KiB blocks");
     static_assert(!(SPLIT && CAUSAL), "split-KV is non-causal");
     static_assert(!PP || (WAVES == 8 && !CAUSAL && !SPLIT), "ping-pong: 8 waves, non-causal");
@@ -166,6 +169,18 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     }
     auto issue_tile = [&](int j, lds_u8* stage) {
         const int soff = j * BC * RB;
+#if defined(FA_LDS_POISON)
+        // Debug build: the 16 bytes each copy below will deliver first hold NaN (all-ones
+        // bits, NaN in bf16, fp16 and fp32), so a read that races its copy -- a missing wait
+        // or barrier -- turns into NaN outputs instead of stale, plausible data.
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            lds_u8* kdst = stage + i * (NT * 16) + wave * 1024 + lane * 16;
+            *reinterpret_cast<lds_u32x4*>(kdst) = u32x4{~0u, ~0u, ~0u, ~0u};
+            *reinterpret_cast<lds_u32x4*>(kdst + TILE) = u32x4{~0u, ~0u, ~0u, ~0u};
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the poison lands before the copies
+#endif
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             lds_u8* kdst = stage + i * (NT * 16) + wave * 1024;
@@ -239,7 +254,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         }
 
         // ---- P = 2^(s*c - m), packed; the O divisor sums the rounded values, LSE the fp32
-        // ones.  P is first formed with the running maximum m as it stands: the exact softmax
+        // ones (fp16: the rounded sum serves both).  P is first formed with the running maximum m as it stands: the exact softmax
         // does not depend on m, which only has to keep P finite and in range.  A tile is
         // redone with its own maximum when some row's tile sum leaves [0, 2^15] -- the first
         // tile (m = -inf), or a row maximum that jumped by more than 15 in base-2 units.
@@ -251,8 +266,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                 float p[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(s[kb][t], c, neg_m));
+                if constexpr (!ONE_SUM) {
 #pragma unroll
-                for (int t = 0; t < 16; t += 2) { acc0 += p[t]; acc1 += p[t + 1]; }
+                    for (int t = 0; t < 16; t += 2) { acc0 += p[t]; acc1 += p[t + 1]; }
+                }
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     u32x4 f;
@@ -268,7 +285,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         };
         make_p(-m);
         // (NaN, from -inf scores against m = -inf, also fails the test)
-        if (__builtin_amdgcn_ballot_w64(!(acc0 + acc1 <= kMaxTileSum)) != 0) {
+        if (__builtin_amdgcn_ballot_w64(!((ONE_SUM ? racc0 + racc1 : acc0 + acc1) <= kMaxTileSum)) != 0) {
             float x0 = -INFINITY, x1 = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -289,7 +306,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                 for (int t = 0; t < 16; ++t) o[db][t] *= alpha;
             make_p(-m);
         }
-        lsum += acc0 + acc1;
+        if constexpr (!ONE_SUM) lsum += acc0 + acc1;
         lrnd += racc0 + racc1;
     };
     // O^T += V_j^T P^T
@@ -379,8 +396,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     }
 
     // ---- epilogue: O / l, LSE = (m + log2 l) ln 2
-    const float lt = pair_sum(lsum);
-    const float inv = 1.0f / pair_sum(lrnd);
+    const float lr = pair_sum(lrnd);
+    const float lt = ONE_SUM ? lr : pair_sum(lsum);
+    const float inv = 1.0f / lr;
     if (SPLIT) {   // normalised fp32 partials of this key range (an empty range: O 0, LSE -inf)
         if (query < N) {
             const bool empty = t0 >= n_tiles;

@@ -72,7 +72,8 @@ constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, 32 CUs 
 constexpr int kCus = 256;
 constexpr int kLdsPerCu = 160 * 1024;
 
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// ceil(a / b) for a >= 0, b > 0, without forming a + b - 1 (no overflow near INT64_MAX)
+inline int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
 
 // LDS bytes of one forward workgroup: a K tile and a V tile per stage.
 inline int fwd_lds_bytes(int dtype, int d, int block_k, int stages) {

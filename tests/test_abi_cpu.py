@@ -493,3 +493,25 @@ def test_log_prints_the_plan_to_stderr(lib, monkeypatch, capfd):
     assert "fa_fwd_fp8: B=1 H=2 N=100 d=128" in err
     assert "Br=128 Bc=64 waves=4 grid=16384 lds=65536 (FA_TILE)" in err
     assert "N=77" not in err          # FA_LOG=0: silent
+
+
+def test_huge_sizes_are_rejected_without_overflow(lib):
+    # sizes near INT64_MAX: every check must reject them without forming an overflowing
+    # product (the sanitized build of the library runs this file under UBSan)
+    big = (1 << 63) - 1
+    assert _fwd(lib, N=big, d=128) == 2
+    assert _fwd(lib, N=1 << 60, d=64) == 2
+    assert _fwd(lib, B=big, H=big) == 2
+    assert _fwd(lib, B=1 << 40, H=1 << 40, N=1 << 40) == 2
+    assert _bwd(lib, N=big, d=128) == 2
+    assert lib.fa_bwd_workspace_bytes(big, big, big, 128, fa.FA_BF16) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, big, 128, fa.FA_BF16, 4) == 0
+    assert lib.fa_fwd_splitkv_qk_workspace_bytes(1, 1, 1, big, 128, fa.FA_BF16, 0) == 0
+    assert _skv_qk(lib, Nk=big) == 2
+    assert lib.fa_fp8_padded_len(big) == 0 and lib.fa_fp8_padded_len(big - 127) == 0
+    assert lib.fa_fp8_padded_len(big - 128) == big - 127   # (2^63 - 129) rounded up to 128
+    assert lib.fa_fp8_scale_blocks(big) == big // 64 + 1
+    assert _q8(lib, N=big) == 2
+    assert _f8(lib, N=big) == 2
+    plan = fa.Plan()
+    assert lib.fa_fwd_plan(big, big, big, 128, fa.FA_BF16, 0, ctypes.byref(plan)) == 2
