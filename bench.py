@@ -30,6 +30,8 @@ ONE JSON line on stdout (everything else goes to stderr):
              d64 (latency-bound), bf16 B4 H16 N2048 d64, fp16 B1 H32 N16384 d128 and the edge
              workload bf16 B2 H8 N4097 d128 (zero, x10 and one-hot heads); median and min of
              per-launch events, TFLOP/s and % of the MFMA peak of the input type
+  causal     the causal forward (fa_fwd_causal) on the same tensors, TFLOP/s counted on the
+             computed half (2*B*H*N^2*d)
   hbm_small_n  short sequences at B*H = 1024, d = 128, bf16, N in {128, 256, 512}, where the
              forward is bounded by HBM: algorithmic bytes (Q, K, V read once, O and LSE
              written once) per launch time, as GB/s and % of the 8 TB/s HBM peak
@@ -423,6 +425,26 @@ def hbm_small_n_leg(fa, stream, steps=20):
     return rows
 
 
+def causal_leg(fa, q, k, v, scale, stream, steps=10):
+    """The causal forward (fa_fwd_causal) on the same tensors; TFLOP/s counted on the half of
+    the score matrix that is computed, 2*B*H*N^2*d."""
+    import statistics
+
+    import torch
+
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], device=q.device, dtype=torch.float32)
+    t = launch_times(lambda: fa.fa_fwd_causal(q, k, v, o, lse, scale=scale, stream=stream), stream, steps, warmup=2)
+    tmed = statistics.median(t)
+    flops = 2.0 * B * H * N * N * D
+    tf = flops / (tmed * 1e-3) / 1e12
+    ok = bool(torch.isfinite(o).all().item() and torch.isfinite(lse).all().item())
+    log(f"causal forward: median {tmed:.3f} ms, {tf:.1f} TFLOP/s on the computed half, finite={ok}")
+    return {"median_ms": round(tmed, 4), "min_ms": round(min(t), 4), "tflops": round(tf, 2),
+            "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "flops": flops,
+            "plan": fa.fa_fwd_plan(B, H, N, D, q.dtype, causal=True), "outputs_finite": ok}
+
+
 def sweep(fa, stream, steps=20):
     """Forward timings of the smaller workloads, the bandwidth-bound short sequences, a decode
     shape, and one small call replayed from a captured graph."""
@@ -516,6 +538,7 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time the smaller workloads")
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' forward timings")
     ap.add_argument("--no-hbm-small-n", action="store_true", help="skip the short-sequence HBM leg")
+    ap.add_argument("--no-causal", action="store_true", help="skip the causal forward leg")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--fp8-steps", type=int, default=10)
     ap.add_argument("--power-seconds", type=float, default=4.0,
@@ -613,6 +636,13 @@ def main():
             "traffic": traffic,
         },
     }
+    # the shorter legs run first, before the sustained power, backward and fp8 legs heat the chip
+    if not args.no_configs:
+        out["configs"] = configs_leg(fa, stream)
+    if not args.no_hbm_small_n:
+        out["hbm_small_n"] = hbm_small_n_leg(fa, stream)
+    if not args.no_causal:
+        out["causal"] = causal_leg(fa, q, k, v, scale, stream)
     if args.power_seconds > 0:
         pw = power_while_running(lambda: fa.fa_fwd(q, k, v, o, lse, scale=scale, stream=stream), args.power_seconds)
         if pw is not None:
@@ -626,10 +656,6 @@ def main():
         out["backward"], grads = time_backward(fa, q, k, v, o, lse, scale, stream, args.backward_steps)
     if not args.no_fp8:
         out["fp8"] = time_fp8(fa, q, k, v, o, scale, stream, args.fp8_steps)
-    if not args.no_configs:
-        out["configs"] = configs_leg(fa, stream)
-    if not args.no_hbm_small_n:
-        out["hbm_small_n"] = hbm_small_n_leg(fa, stream)
     if args.sweep:
         out["sweep"] = sweep(fa, stream)
     if not args.no_cpu_baseline:

@@ -283,9 +283,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                 }
             }
         };
-        make_p(-m);
-        // (NaN, from -inf scores against m = -inf, also fails the test)
-        if (__builtin_amdgcn_ballot_w64(!((ONE_SUM ? racc0 + racc1 : acc0 + acc1) <= kMaxTileSum)) != 0) {
+        // The workgroup's first tile meets m = -inf, which would fail the test anyway: it takes
+        // its own maximum at once.  (NaN, from -inf scores against m = -inf, fails the test.)
+        bool redo = true;
+        if (j != t0) {
+            make_p(-m);
+            redo = __builtin_amdgcn_ballot_w64(!((ONE_SUM ? racc0 + racc1 : acc0 + acc1) <= kMaxTileSum)) != 0;
+        }
+        if (redo) {
             float x0 = -INFINITY, x1 = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)

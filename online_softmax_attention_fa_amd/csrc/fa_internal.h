@@ -90,9 +90,38 @@ inline int fwd_lds_bytes(int dtype, int d, int block_k, int stages) {
 // copied; two otherwise.
 inline int fwd_stages(int d, int waves, int causal) { return (waves == 8 && d == 64 && !causal) ? 3 : 2; }
 
+// Relative throughput of one CU running m resident forward workgroups (index m), measured
+// across grids of one to three rounds at N = 2049..4097 and the long workloads: a lone 4-wave
+// workgroup (one wave per SIMD) cannot overlap its own softmax with its MFMAs; two or three
+// overlap each other's; one 8-wave workgroup (two waves per SIMD, half the L2 -> LDS traffic
+// per FLOP) runs as well as three 4-wave ones.
+constexpr double kEff4[4] = {0.0, 0.6, 1.0, 1.05};
+constexpr double kEff8[2] = {0.0, 1.05};
+
+// Time of a grid of w workgroups of `unit` work each (1 = 256 query rows against all keys),
+// at most per_cu resident per CU: whole rounds of per_cu per CU, then a last partial round
+// whose busiest CU holds ceil(rem / kCus) of them.
+inline double grid_time(int64_t w, double unit, int per_cu, const double* eff) {
+    const int64_t slots = (int64_t)per_cu * kCus;
+    const int64_t full = w / slots, rem = w % slots;
+    double t = (double)full * per_cu * unit / eff[per_cu];
+    if (rem) {
+        const int m = (int)ceil_div(rem, kCus);
+        t += m * unit / eff[m];
+    }
+    return t;
+}
+
 // The chooser.  Inputs are already validated (d in {64,128}, dtype known, N > 0).
 //
 // bf16/fp16: 32 query rows per wave (one 32-row MFMA column block), two waves per SIMD.
+//  * Non-causal, N >= 2048: the plan grid_time costs lowest, over 8 waves (Br = 256), 4 waves
+//    at two workgroups per CU and 4 waves at three.  It picks the measured best plan on every
+//    grid tried: 8 waves for full rounds (B4 H32 N16384), for B3 H8 N4097 (408 blocks of 256;
+//    218 against 233-238 us) and B2 H8 N2049 (58 against 62-63 us); three 4-wave workgroups
+//    per CU for B2 H8 N4097 (176 against 190-201 us), B4 H8 N4097 (288 against 304-307 us)
+//    and d = 64 B2 H16 N4097 (180 against 196 us); 4 waves at two per CU for B1 H8 N4096.
+//    The rules below serve causal grids and shorter heads.
 //  * Long sequences: 8 waves per workgroup (Br = 256, one workgroup per CU) and Bc = 128
 //    keys per LDS stage (128 KiB of K/V stages at d = 128).  A K/V tile then serves twice
 //    as many queries -- half the L2 -> LDS traffic per FLOP -- with half as many
@@ -129,6 +158,20 @@ inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int d
     if (dtype == FA_F32) {
         p.block_k = 32;
         p.wave_kv_splits = 4;
+    } else if (!causal && N >= 2048) {
+        // Three plans, costed by grid_time: 8 waves (one 256-row workgroup per CU), 4 waves at
+        // two workgroups per CU (Bc 64 at d = 128, 128 at d = 64) or at three (Bc 32 / 64).
+        const int64_t g8 = B * H * ceil_div(N, 8 * 32), g4 = B * H * ceil_div(N, 4 * 32);
+        const double t8 = grid_time(g8, 1.0, 1, kEff8);
+        const double t2 = grid_time(g4, 0.5, 2, kEff4);
+        const double t3 = grid_time(g4, 0.5, 3, kEff4);
+        if (t8 <= t2 && t8 <= t3) {
+            p.waves = 8;
+            p.block_k = 128;
+        } else {
+            p.waves = 4;
+            p.block_k = t2 <= t3 ? (d == 128 ? 64 : 128) : (d == 128 ? 32 : 64);
+        }
     } else {
         const int64_t g8 = B * H * ceil_div(N, 8 * 32);   // workgroups at Br = 256
         const bool eight = N >= 2048 && (g8 >= 2 * kCus || g8 % kCus == 0);

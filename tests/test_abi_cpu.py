@@ -185,8 +185,31 @@ def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_sh
     assert (p["waves"], p["block_k"], p["lds_bytes"]) == (4, 64, 32768)
     assert fa.fa_fwd_plan(1, 8, 512, 64, fa.FA_BF16)["block_k"] == 128
     assert fa.fa_fwd_plan(16, 64, 512, 64, fa.FA_BF16, causal=True)["block_k"] == 128
-    assert fa.fa_fwd_plan(3, 6, 3000, 128, fa.FA_BF16)["block_k"] == 64
-    assert fa.fa_fwd_plan(2, 8, 4097, 64, fa.FA_BF16)["block_k"] == 128
+    # under one round of 256-row blocks: one 8-wave workgroup per CU on 216 CUs beats 432
+    # four-wave ones at up to two per CU
+    p = fa.fa_fwd_plan(3, 6, 3000, 128, fa.FA_BF16)
+    assert (p["waves"], p["block_k"], p["grid"]) == (8, 128, 216)
+    # d = 64, 528 blocks of 128 rows: three per CU in one round (as at d = 128)
+    p = fa.fa_fwd_plan(2, 8, 4097, 64, fa.FA_BF16)
+    assert (p["waves"], p["block_k"], p["grid"]) == (4, 64, 528)
+
+
+@pytest.mark.parametrize("B,H,N,d,plan", [
+    # (waves, Bc): the measured best plan of each grid (interleaved timings on one MI355X)
+    (4, 32, 16384, 128, (8, 128)),   # 32 full rounds of 256-row blocks
+    (3, 8, 4097, 128, (8, 128)),     # 408 blocks of 256: 218 us; 4 waves 233-238 us
+    (2, 8, 2049, 128, (8, 128)),     # 144 blocks of 256: 58 us; 4 waves 62-63 us
+    (2, 8, 4000, 128, (8, 128)),     # 256 blocks of 256: 125 us; 4 waves 133-134 us
+    (2, 8, 4097, 128, (4, 32)),      # 528 blocks of 128 at three per CU: 176 us; others 190-201 us
+    (4, 8, 4097, 128, (4, 32)),      # 1056 blocks of 128: 288 us; others 304-307 us
+    (1, 16, 4097, 128, (4, 32)),     # 528 blocks of 128: 166 us; others 183-184 us
+    (2, 16, 4097, 64, (4, 64)),      # d = 64, 1056 blocks: 180 us; 8 waves 196 us, 2 per CU 187 us
+    (1, 8, 4096, 128, (4, 64)),      # 256 blocks of 128, one per CU: 80 us; 8 waves 100 us
+    (4, 16, 2048, 64, (8, 128)),     # 512 blocks of 256 (ping-pong): 84 us; 4 waves 86-87 us
+])
+def test_plan_cost_model_picks_the_measured_best_plan(lib, B, H, N, d, plan):
+    p = fa.fa_fwd_plan(B, H, N, d, fa.FA_BF16)
+    assert (p["waves"], p["block_k"]) == plan
 
 
 def test_plan_validates_like_fwd(lib):

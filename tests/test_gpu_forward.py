@@ -115,13 +115,15 @@ def test_large_magnitude_scores(gpu_lib, dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_large_magnitude_scores_eight_wave_plans(gpu_lib, dtype, d, causal):
+def test_large_magnitude_scores_eight_wave_plans(gpu_lib, monkeypatch, dtype, d, causal):
     # Scores of several hundred on the long-sequence plans (8 waves; at d = 64 non-causal the
     # ping-pong schedule; causal d = 128 the 32-key plan): the running maximum jumps on later
-    # tiles too, so tiles are redone with their own maximum, next to the diagonal masks.
+    # tiles too, so tiles are redone with their own maximum, next to the diagonal masks.  The
+    # plan is pinned through FA_TILE (the chooser picks by grid size).
     import torch
 
     B, H, N = 4, 16, 2100
+    monkeypatch.setenv("FA_TILE", "128,32,4" if causal and d == 128 else "256,128,8")
     plan = gpu_lib.fa_fwd_plan(B, H, N, d, wl_dtype_code(dtype), causal=causal)
     assert plan["waves"] == (4 if causal and d == 128 else 8)
     sigma = 10.0 if dtype == "bf16" else 4.0
@@ -212,13 +214,14 @@ def test_empty_problem_is_a_no_op(gpu_lib):
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N,causal", [(2049, False), (3000, False), (8191, False), (2500, True), (4099, True)])
-def test_eight_wave_plan_sampled(gpu_lib, dtype, d, N, causal):
-    # B*H = 64 puts these on the 8-wave, 128-key-tile plan (causal at d = 128: the 4-wave,
-    # 32-key-tile plan at three waves per SIMD); rows past the last full query block and keys
+def test_eight_wave_plan_sampled(gpu_lib, monkeypatch, dtype, d, N, causal):
+    # The 8-wave, 128-key-tile plan (causal at d = 128: the 4-wave, 32-key-tile plan at three
+    # waves per SIMD), pinned through FA_TILE; rows past the last full query block and keys
     # past the last full tile exercise the masks.
     import torch
 
     B, H = 4, 16
+    monkeypatch.setenv("FA_TILE", "128,32,4" if causal and d == 128 else "256,128,8")
     plan = gpu_lib.fa_fwd_plan(B, H, N, d, wl_dtype_code(dtype), causal=causal)
     if causal and d == 128:
         assert plan["waves"] == 4 and plan["block_k"] == 32

@@ -114,16 +114,22 @@ def test_fp8_and_causal_in_one_graph(gpu_lib):
             assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}: {name} differs"
 
 
-def test_ping_pong_and_short_head_forwards_in_one_graph(gpu_lib):
-    """The d = 64 ping-pong schedule (8-wave plan, three stages) and the three-per-CU
-    short-head plans (d = 64 and d = 128) captured together; every replay must reproduce
-    the eager results bit for bit."""
+def test_ping_pong_and_short_head_forwards_in_one_graph(gpu_lib, monkeypatch):
+    """The d = 64 ping-pong schedule (8-wave plan, three stages; pinned through FA_TILE) and
+    the three-per-CU short-head plans (d = 64 and d = 128) captured together; every replay
+    must reproduce the eager results bit for bit."""
+    import os
+
     import torch
 
     fa = gpu_lib
     gen = torch.Generator(device="cuda").manual_seed(37)
     shapes = ((4, 16, 2100, 64), (16, 32, 300, 64), (16, 32, 300, 128))
-    plans = [fa.fa_fwd_plan(*sh, torch.bfloat16) for sh in shapes]
+    tiles = ("256,128,8", "", "")     # the library reads FA_TILE at each call
+    plans = []
+    for sh, tile in zip(shapes, tiles):
+        monkeypatch.setenv("FA_TILE", tile)
+        plans.append(fa.fa_fwd_plan(*sh, torch.bfloat16))
     assert (plans[0]["waves"], plans[0]["block_k"]) == (8, 128)
     assert (plans[1]["waves"], plans[1]["block_k"]) == (4, 64)
     assert (plans[2]["waves"], plans[2]["block_k"]) == (4, 32)
@@ -132,7 +138,8 @@ def test_ping_pong_and_short_head_forwards_in_one_graph(gpu_lib):
     outs = [(torch.empty_like(q), torch.empty(q.shape[:3], device="cuda", dtype=torch.float32)) for q, _, _ in ins]
 
     def work(stream):
-        for (q, k, v), (o, lse) in zip(ins, outs):
+        for (q, k, v), (o, lse), tile in zip(ins, outs, tiles):
+            os.environ["FA_TILE"] = tile
             fa.fa_fwd(q, k, v, o, lse, stream=stream)
 
     work(torch.cuda.current_stream())
