@@ -422,8 +422,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         }
         return;
     }
-    if (query < N) {
-        T* orow = Oh + (int64_t)query * D;
+    // O leaves through LDS: each wave writes its 32 rows there in the accumulator layout (one
+    // row per lane, 8-byte pieces) and reads them back 16 bytes per lane along the rows, so
+    // every global store instruction writes whole contiguous rows instead of 8-byte pieces
+    // of 32 rows.  The stages are free once every wave has passed this barrier (in the
+    // ping-pong schedule the late group's last P V reads a stage after its last tile barrier).
+    __syncthreads();
+    if (has_rows) {
+        constexpr int WPS = BC / 16;               // waves whose 32 rows fit in one stage
+        lds_u8* obuf = (wave / WPS == 0 ? stage0 : stage1) + (wave % WPS) * (QPW * RB);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -431,9 +438,21 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                 u32x2 w;
                 w[0] = Elt<T>::pack2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
                 w[1] = Elt<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = w;
+                *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+                    obuf + l32 * RB + 16 * ((4 * db + g) ^ swz<CPR>(l32)) + 8 * h) = w;
             }
-        if (h == 0) Lh[query] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+        // the wave reads back what its other lanes wrote
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        constexpr int LPR = RB / 16, RPI = 64 / LPR;   // lanes per row, rows per instruction
+#pragma unroll
+        for (int k = 0; k < QPW / RPI; ++k) {
+            const int row = k * RPI + lane / LPR, ch = lane % LPR;
+            const u32x4 v = lds_read16(obuf, row * RB + 16 * (ch ^ swz<CPR>(row)));
+            if (q_wave + row < N) *reinterpret_cast<u32x4*>(Oh + (int64_t)(q_wave + row) * D + ch * 8) = v;
+        }
+        if (h == 0 && query < N) Lh[query] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
     }
 #endif
 }
