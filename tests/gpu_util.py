@@ -138,9 +138,13 @@ def compare_grad(G, G_ref, dtype: str, what: str = "", mass=None, check_fro: boo
     den = np.linalg.norm(G_ref)
     rel = float(np.linalg.norm(G - G_ref) / den) if den > 0 else float(np.linalg.norm(G))
     ratio = err / bound
+    # the O rule (tolerance + half an output ulp), reported beside the derived bound
+    o_rule = O_TOL[dtype] + half_ulp(G_ref, dtype)
     summary = dict(max_err=float(err.max()) if err.size else 0.0, rel_fro=rel,
                    max_err_over_bound=float(ratio.max()) if ratio.size else 0.0,
-                   max_ref=float(np.abs(G_ref).max()) if G_ref.size else 0.0)
+                   max_ref=float(np.abs(G_ref).max()) if G_ref.size else 0.0,
+                   max_err_over_o_rule=float((err / o_rule).max()) if err.size else 0.0,
+                   n_above_o_rule=int((err > o_rule).sum()))
     if bad.any():
         idx = np.unravel_index(np.argmax(ratio), err.shape)
         raise AssertionError(f"{what}: error {err[idx]:.3e} > bound {bound[idx]:.3e} at {idx} "

@@ -180,23 +180,33 @@ def test_backward_large_workload_sampled(gpu_lib):
     torch.cuda.synchronize()
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all().item()
-    worst = {}
+    worst = {"dQ": {}, "dK": {}, "dV": {}}
+
+    def keep(name, s):
+        worst[name] = {key: max(worst[name].get(key, 0), val) for key, val in s.items()}
+
     for b in range(w.B):
         for h in range(w.H):
             rows = wl.sampled_rows(w, b, h)
             rr = torch.from_numpy(rows).cuda()
             ref, m = _rows_ref(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, rows, w.dtype)
-            s = compare_grad(to_host(dq[b, h].index_select(0, rr)), ref, w.dtype, f"b{b} h{h} dQ", mass=m)
-            worst = {key: max(worst.get(key, 0), val) for key, val in s.items()}
+            keep("dQ", compare_grad(to_host(dq[b, h].index_select(0, rr)), ref, w.dtype, f"b{b} h{h} dQ", mass=m))
     rng = np.random.default_rng([w.cid, 7])
     heads = [(int(x) // w.H, int(x) % w.H) for x in rng.choice(w.B * w.H, size=3, replace=False)]
     for b, h in heads:
         cols = wl.sampled_rows(w, b, h)
         cc = torch.from_numpy(cols).cuda()
         dk_ref, dv_ref, m_dk, m_dv = _cols_ref(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, cols, w.dtype)
-        compare_grad(to_host(dk[b, h].index_select(0, cc)), dk_ref, w.dtype, f"b{b} h{h} dK", mass=m_dk)
-        compare_grad(to_host(dv[b, h].index_select(0, cc)), dv_ref, w.dtype, f"b{b} h{h} dV", mass=m_dv)
-    print(f"{w.name}: dQ worst {worst}; dK/dV heads {heads}")
+        keep("dK", compare_grad(to_host(dk[b, h].index_select(0, cc)), dk_ref, w.dtype, f"b{b} h{h} dK", mass=m_dk))
+        keep("dV", compare_grad(to_host(dv[b, h].index_select(0, cc)), dv_ref, w.dtype, f"b{b} h{h} dV", mass=m_dv))
+    # bare max-abs errors next to the derived bound and the O rule (1e-2 + half an ulp): the
+    # distance to each, over every sampled row (dQ, all heads) and column (dK, dV, 3 heads)
+    for name, s in worst.items():
+        print(f"{w.name} {name}: max |err| {s['max_err']:.3e} (max |ref| {s['max_ref']:.3e}), "
+              f"{s['max_err_over_bound']:.3f} of the derived bound, {s['max_err_over_o_rule']:.3f} of 1e-2 + half ulp "
+              f"({s['n_above_o_rule']} above), relative Frobenius {s['rel_fro']:.2e}")
+        assert s["n_above_o_rule"] == 0, f"{name}: {s}"
+    print(f"dK/dV heads {heads}")
 
 
 _rng = np.random.default_rng(20261203)
