@@ -431,6 +431,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     if (has_rows) {
         constexpr int WPS = BC / 16;               // waves whose 32 rows fit in one stage
         lds_u8* obuf = (wave / WPS == 0 ? stage0 : stage1) + (wave % WPS) * (QPW * RB);
+        // Staging layout: 16-byte chunk c of row r sits in slot c ^ ochunk(r) and its two
+        // 8-byte halves are swapped when ohalf(r) is set.  A write instruction puts one
+        // 8-byte piece of each of the wave's 32 rows; with this layout the pieces of any 16
+        // consecutive lanes fill 128 distinct bytes modulo 128, those of 32 lanes 256
+        // distinct bytes modulo 256, and lanes r and r + 32 share a slot, so the writes are
+        // free of bank conflicts however the LDS groups lanes.  A read of 16 bytes along a row
+        // still covers one row's slots exactly once per group of lanes.
+        auto ochunk = [](int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); };
+        auto ohalf = [](int r) { return CPR == 16 ? ((r >> 3) ^ (r >> 4)) & 1 : (r ^ (r >> 4)) & 1; };
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -439,18 +448,26 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                 w[0] = Elt<T>::pack2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
                 w[1] = Elt<T>::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
                 *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
-                    obuf + l32 * RB + 16 * ((4 * db + g) ^ swz<CPR>(l32)) + 8 * h) = w;
+                    obuf + l32 * RB + 16 * ((4 * db + g) ^ ochunk(l32)) + 8 * (h ^ ohalf(l32))) = w;
             }
         // the wave reads back what its other lanes wrote
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        constexpr int LPR = RB / 16, RPI = 64 / LPR;   // lanes per row, rows per instruction
+        constexpr int LPR = RB / 16, RPI = 64 / LPR, NR = QPW / RPI;   // lanes per row, rows per read, reads
+        const int ch = lane % LPR;
+        u32x4 v[NR];
 #pragma unroll
-        for (int k = 0; k < QPW / RPI; ++k) {
-            const int row = k * RPI + lane / LPR, ch = lane % LPR;
-            const u32x4 v = lds_read16(obuf, row * RB + 16 * (ch ^ swz<CPR>(row)));
-            if (q_wave + row < N) *reinterpret_cast<u32x4*>(Oh + (int64_t)(q_wave + row) * D + ch * 8) = v;
+        for (int k = 0; k < NR; ++k) {   // every read in flight before the first store
+            const int row = k * RPI + lane / LPR;
+            v[k] = lds_read16(obuf, row * RB + 16 * (ch ^ ochunk(row)));
+        }
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int row = k * RPI + lane / LPR;
+            const u32x4 x = ohalf(row) ? u32x4{v[k][2], v[k][3], v[k][0], v[k][1]} : v[k];
+            if (q_wave + QPW <= N || q_wave + row < N)
+                *reinterpret_cast<u32x4*>(Oh + (int64_t)(q_wave + row) * D + ch * 8) = x;
         }
         if (h == 0 && query < N) Lh[query] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
     }
