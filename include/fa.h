@@ -24,7 +24,8 @@
  *     ((b*H + h)*N + n)*d + k.  LSE / D are contiguous fp32 [B, H, N].
  *   - Q, K, V, O (and dO, dQ, dK, dV) share one element type `dtype`; O has the
  *     input dtype.  LSE is always fp32, natural log.
- *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  The header declares the
+ *     type as HIP does, an opaque pointer, so it needs no HIP header of its own.
  *     Calls are asynchronous: validation errors return synchronously before any
  *     work is queued; device faults surface at the caller's next synchronisation.
  *   - Outputs must not alias inputs.  Tensor pointers must be 16-byte aligned,
@@ -60,6 +61,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* HIP's stream handle, declared exactly as hip_runtime_api.h declares it (an identical
+ * typedef may appear twice), so that callers without HIP headers can still pass one. */
+typedef struct ihipStream_t* hipStream_t;
 
 /* Compiled as C++, the enumerations take int as their fixed underlying type, so any int a
  * C caller passes (an unknown dtype, an unknown status) is a valid value for the library to
@@ -116,7 +121,7 @@ typedef struct {
  */
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                 fa_dtype dtype, void* stream);
+                 fa_dtype dtype, hipStream_t stream);
 
 /*
  * Causal forward: as fa_fwd, but query i attends only to keys j <= i (the
@@ -125,7 +130,7 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
  */
 fa_status fa_fwd_causal(const void* Q, const void* K, const void* V, void* O, float* LSE,
                         int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                        fa_dtype dtype, void* stream);
+                        fa_dtype dtype, hipStream_t stream);
 
 /*
  * The plan fa_fwd / fa_fwd_causal would launch for this problem on a gfx950
@@ -156,7 +161,7 @@ size_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d
 int32_t fa_fwd_splitkv_splits(int64_t B, int64_t H, int64_t N, int64_t d, fa_dtype dtype);
 fa_status fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
                          void* workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
-                         float scale, fa_dtype dtype, int32_t splits, void* stream);
+                         float scale, fa_dtype dtype, int32_t splits, hipStream_t stream);
 
 /*
  * The same with Nq query rows and Nk keys per head (Q, O [B,H,Nq,d]; K, V [B,H,Nk,d]; LSE
@@ -172,7 +177,7 @@ int32_t fa_fwd_splitkv_qk_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, i
 fa_status fa_fwd_splitkv_qk(const void* Q, const void* K, const void* V, void* O, float* LSE,
                             void* workspace, size_t ws_bytes, int64_t B, int64_t H, int64_t Nq,
                             int64_t Nk, int64_t d, float scale, fa_dtype dtype, int32_t splits,
-                            void* stream);
+                            hipStream_t stream);
 
 /*
  * fa_fwd_splitkv_qk without a workspace argument and without any allocation, for callers
@@ -191,7 +196,7 @@ fa_status fa_fwd_splitkv_qk(const void* Q, const void* K, const void* V, void* O
  */
 fa_status fa_fwd_splitkv_qk_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
-                                    fa_dtype dtype, int32_t splits, void* stream);
+                                    fa_dtype dtype, int32_t splits, hipStream_t stream);
 
 /*
  * Workspace the backward needs, in bytes: two fp32 values per row (B*H*N rows).
@@ -215,13 +220,13 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dty
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                  const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t ws_bytes,
                  int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
-                 void* stream);
+                 hipStream_t stream);
 
 /* Backward of fa_fwd_causal (keys after the query row get P = 0). */
 fa_status fa_bwd_causal(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                         const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t ws_bytes,
                         int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
-                        void* stream);
+                        hipStream_t stream);
 
 /*
  * Block-scaled fp8 mode (opt-in; changes the numerics).  "从零理解Flash Attention中的online
@@ -253,7 +258,7 @@ int64_t fa_fp8_scale_blocks(int64_t N);
  * 4-byte aligned); transpose not 0/1 -> FA_ERR_UNSUPPORTED.
  */
 fa_status fa_quantize_fp8(const void* X, void* X8, float* scales, int64_t B, int64_t H, int64_t N,
-                          int64_t d, fa_dtype dtype, int32_t transpose, void* stream);
+                          int64_t d, fa_dtype dtype, int32_t transpose, hipStream_t stream);
 /*
  * Attention forward on block-scaled E4M3 inputs: Q8, K8 [B,H,N,d] codes, Vt8 [B,H,d,Np]
  * codes, their scales [B,H,nb]; writes O [B,H,N,d] of out_dtype (FA_BF16 / FA_F16) and
@@ -263,14 +268,14 @@ fa_status fa_quantize_fp8(const void* X, void* X8, float* scales, int64_t B, int
  */
 fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale,
                      const float* k_scale, const float* v_scale, void* O, float* LSE, int64_t B,
-                     int64_t H, int64_t N, int64_t d, float scale, fa_dtype out_dtype, void* stream);
+                     int64_t H, int64_t N, int64_t d, float scale, fa_dtype out_dtype, hipStream_t stream);
 /*
  * fa_fwd_fp8 with the causal mask of fa_fwd_causal: query row i attends to keys 0..i.
  * Same arguments, layouts and errors.
  */
 fa_status fa_fwd_fp8_causal(const void* Q8, const void* K8, const void* Vt8, const float* q_scale,
                             const float* k_scale, const float* v_scale, void* O, float* LSE, int64_t B,
-                            int64_t H, int64_t N, int64_t d, float scale, fa_dtype out_dtype, void* stream);
+                            int64_t H, int64_t N, int64_t d, float scale, fa_dtype out_dtype, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(fa_status s);

@@ -107,7 +107,7 @@ fa_status check_problem(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
 // already validated there).
 fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float* LSE,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
-                     void* stream, int causal, int64_t Nk = -1) {
+                     hipStream_t stream, int causal, int64_t Nk = -1) {
     if (Nk < 0) Nk = N;
     fa_status st = check_problem(B, H, N, d, dtype);
     if (st != FA_OK) return st;
@@ -172,7 +172,7 @@ int32_t effective_splits(int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d,
 // ws_bytes are then ignored.
 fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, float* LSE, void* ws,
                          size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d, float scale,
-                         fa_dtype dtype, int32_t splits, void* stream, bool use_scratch = false) {
+                         fa_dtype dtype, int32_t splits, hipStream_t stream, bool use_scratch = false) {
     fa_status st = check_splitkv(B, H, N, Nk, d, dtype, splits);
     if (st != FA_OK) return st;
     if (B * H * N == 0) return FA_OK;
@@ -236,7 +236,7 @@ fa_status check_fp8_problem(int64_t B, int64_t H, int64_t N, int64_t d, int dtyp
 fa_status bwd_common(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                      const float* LSE, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
-                     void* stream, int causal) {
+                     hipStream_t stream, int causal) {
     fa_status st = check_problem(B, H, N, d, dtype);
     if (st != FA_OK) return st;
     if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
@@ -293,13 +293,13 @@ int32_t fa_fwd_splitkv_qk_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, i
 
 fa_status fa_fwd_splitkv_qk(const void* Q, const void* K, const void* V, void* O, float* LSE, void* workspace,
                             size_t ws_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
-                            fa_dtype dtype, int32_t splits, void* stream) {
+                            fa_dtype dtype, int32_t splits, hipStream_t stream) {
     return splitkv_common(Q, K, V, O, LSE, workspace, ws_bytes, B, H, Nq, Nk, d, scale, dtype, splits, stream);
 }
 
 fa_status fa_fwd_splitkv_qk_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
                                     int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, fa_dtype dtype,
-                                    int32_t splits, void* stream) {
+                                    int32_t splits, hipStream_t stream) {
     return splitkv_common(Q, K, V, O, LSE, nullptr, 0, B, H, Nq, Nk, d, scale, dtype, splits, stream,
                           /*use_scratch=*/true);
 }
@@ -314,7 +314,7 @@ int32_t fa_fwd_splitkv_splits(int64_t B, int64_t H, int64_t N, int64_t d, fa_dty
 
 fa_status fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, void* workspace,
                          size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
-                         int32_t splits, void* stream) {
+                         int32_t splits, hipStream_t stream) {
     return splitkv_common(Q, K, V, O, LSE, workspace, ws_bytes, B, H, N, N, d, scale, dtype, splits, stream);
 }
 
@@ -325,7 +325,7 @@ int64_t fa_fp8_padded_len(int64_t N) {
 int64_t fa_fp8_scale_blocks(int64_t N) { return N < 0 ? 0 : fa::fp8_scale_blocks(N); }
 
 fa_status fa_quantize_fp8(const void* X, void* X8, float* scales, int64_t B, int64_t H, int64_t N, int64_t d,
-                          fa_dtype dtype, int32_t transpose, void* stream) {
+                          fa_dtype dtype, int32_t transpose, hipStream_t stream) {
     fa_status st = check_fp8_problem(B, H, N, d, dtype);
     if (st != FA_OK) return st;
     if (transpose != 0 && transpose != 1) return FA_ERR_UNSUPPORTED;
@@ -351,7 +351,7 @@ fa_status fa_quantize_fp8(const void* X, void* X8, float* scales, int64_t B, int
 namespace {
 fa_status fwd_fp8_common(const void* Q8, const void* K8, const void* Vt8, const float* q_scale, const float* k_scale,
                          const float* v_scale, void* O, float* LSE, int64_t B, int64_t H, int64_t N, int64_t d,
-                         float scale, fa_dtype out_dtype, void* stream, int causal) {
+                         float scale, fa_dtype out_dtype, hipStream_t stream, int causal) {
     fa_status st = check_fp8_problem(B, H, N, d, out_dtype);
     if (st != FA_OK) return st;
     if (B * H * N == 0) return FA_OK;
@@ -388,13 +388,13 @@ fa_status fwd_fp8_common(const void* Q8, const void* K8, const void* Vt8, const 
 
 fa_status fa_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, const float* q_scale, const float* k_scale,
                      const float* v_scale, void* O, float* LSE, int64_t B, int64_t H, int64_t N, int64_t d,
-                     float scale, fa_dtype out_dtype, void* stream) {
+                     float scale, fa_dtype out_dtype, hipStream_t stream) {
     return fwd_fp8_common(Q8, K8, Vt8, q_scale, k_scale, v_scale, O, LSE, B, H, N, d, scale, out_dtype, stream, 0);
 }
 
 fa_status fa_fwd_fp8_causal(const void* Q8, const void* K8, const void* Vt8, const float* q_scale,
                             const float* k_scale, const float* v_scale, void* O, float* LSE, int64_t B, int64_t H,
-                            int64_t N, int64_t d, float scale, fa_dtype out_dtype, void* stream) {
+                            int64_t N, int64_t d, float scale, fa_dtype out_dtype, hipStream_t stream) {
     return fwd_fp8_common(Q8, K8, Vt8, q_scale, k_scale, v_scale, O, LSE, B, H, N, d, scale, out_dtype, stream, 1);
 }
 
@@ -405,27 +405,27 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, fa_dty
 
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                  const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t ws_bytes,
-                 int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype, void* stream) {
+                 int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype, hipStream_t stream) {
     return bwd_common(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, ws_bytes, B, H, N, d, scale, dtype, stream, 0);
 }
 
 fa_status fa_bwd_causal(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                         const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t ws_bytes,
                         int64_t B, int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype,
-                        void* stream) {
+                        hipStream_t stream) {
     return bwd_common(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, ws_bytes, B, H, N, d, scale, dtype, stream, 1);
 }
 
 
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                 fa_dtype dtype, void* stream) {
+                 fa_dtype dtype, hipStream_t stream) {
     return fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, dtype, stream, 0);
 }
 
 fa_status fa_fwd_causal(const void* Q, const void* K, const void* V, void* O, float* LSE,
                         int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                        fa_dtype dtype, void* stream) {
+                        fa_dtype dtype, hipStream_t stream) {
     return fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, dtype, stream, 1);
 }
 

@@ -500,9 +500,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int64_t rows, int causal, hipSt
 
 }  // namespace fa
 
-int fa_launch_bwd(const fa::BwdArgs& a, int64_t rows, int dtype, int d, int causal, void* stream) {
+int fa_launch_bwd(const fa::BwdArgs& a, int64_t rows, int dtype, int d, int causal, hipStream_t st) {
     using namespace fa;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == FA_BF16) e = d == 128 ? launch_bwd_t<__bf16, 128>(a, rows, causal, st) : launch_bwd_t<__bf16, 64>(a, rows, causal, st);
     else e = d == 128 ? launch_bwd_t<_Float16, 128>(a, rows, causal, st) : launch_bwd_t<_Float16, 64>(a, rows, causal, st);

@@ -52,6 +52,6 @@ constexpr int kFp8BlockQ = 128;
 
 // Launchers implemented in fa_fp8_kernel.hip (0 or the hipError_t of the launch).
 // in_dtype: input type of the quantiser; out_dtype: O's type in the forward.
-int fa_launch_quantize_fp8(const fa::QuantArgs& a, int64_t bh, int in_dtype, int d, int transpose, void* stream);
-int fa_launch_fwd_fp8(const fa::Fp8Args& a, int out_dtype, int d, int causal, void* stream);
+int fa_launch_quantize_fp8(const fa::QuantArgs& a, int64_t bh, int in_dtype, int d, int transpose, hipStream_t stream);
+int fa_launch_fwd_fp8(const fa::Fp8Args& a, int out_dtype, int d, int causal, hipStream_t stream);
 

@@ -448,28 +448,28 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
 }
 
 template <typename T, int D>
-int launch_quant_t(const QuantArgs& a, int64_t bh, int transpose, void* stream) {
+int launch_quant_t(const QuantArgs& a, int64_t bh, int transpose, hipStream_t stream) {
     const dim3 grid((unsigned)(bh * a.blocks_per_head));
     if (transpose)
-        hipLaunchKernelGGL((quant_fp8_kernel<T, D, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+        hipLaunchKernelGGL((quant_fp8_kernel<T, D, true>), grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((quant_fp8_kernel<T, D, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
+        hipLaunchKernelGGL((quant_fp8_kernel<T, D, false>), grid, dim3(256), 0, stream, a);
     return (int)hipGetLastError();
 }
 
 template <typename TO, int D>
-int launch_fp8_t(const Fp8Args& a, int causal, void* stream) {
+int launch_fp8_t(const Fp8Args& a, int causal, hipStream_t stream) {
     constexpr int WAVES = kFp8BlockQ / 32;
     if (causal)
-        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, WAVES, true>), dim3(a.n_blocks), dim3(64 * WAVES), 0, (hipStream_t)stream, a);
+        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, WAVES, true>), dim3(a.n_blocks), dim3(64 * WAVES), 0, stream, a);
     else
-        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, WAVES, false>), dim3(a.n_blocks), dim3(64 * WAVES), 0, (hipStream_t)stream, a);
+        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, WAVES, false>), dim3(a.n_blocks), dim3(64 * WAVES), 0, stream, a);
     return (int)hipGetLastError();
 }
 
 }  // namespace fa
 
-int fa_launch_quantize_fp8(const fa::QuantArgs& a, int64_t bh, int in_dtype, int d, int transpose, void* stream) {
+int fa_launch_quantize_fp8(const fa::QuantArgs& a, int64_t bh, int in_dtype, int d, int transpose, hipStream_t stream) {
     if (in_dtype == FA_BF16)
         return d == 128 ? fa::launch_quant_t<__bf16, 128>(a, bh, transpose, stream)
                         : fa::launch_quant_t<__bf16, 64>(a, bh, transpose, stream);
@@ -477,7 +477,7 @@ int fa_launch_quantize_fp8(const fa::QuantArgs& a, int64_t bh, int in_dtype, int
                     : fa::launch_quant_t<_Float16, 64>(a, bh, transpose, stream);
 }
 
-int fa_launch_fwd_fp8(const fa::Fp8Args& a, int out_dtype, int d, int causal, void* stream) {
+int fa_launch_fwd_fp8(const fa::Fp8Args& a, int out_dtype, int d, int causal, hipStream_t stream) {
     if (out_dtype == FA_BF16)
         return d == 128 ? fa::launch_fp8_t<__bf16, 128>(a, causal, stream) : fa::launch_fp8_t<__bf16, 64>(a, causal, stream);
     return d == 128 ? fa::launch_fp8_t<_Float16, 128>(a, causal, stream) : fa::launch_fp8_t<_Float16, 64>(a, causal, stream);

@@ -531,7 +531,8 @@ static hipError_t launch_splitkv_t(const FwdArgs& a, int64_t rows, hipStream_t s
 // running m, l and O for the 32 rows and its own K/V tile in LDS.  The four partial
 // states are then merged through LDS with the two-block rule of "FlashAttention
 // 硬件感知计算剖析" (section 二): M = max_w m_w, l = sum_w 2^(m_w - M) l_w,
-// O = sum_w 2^(m_w - M) O_w / l.  Four times fewer tiles run back to back per wave.
+// O = sum_w (2^(m_w - M) / l) O_w, one reciprocal per row.  Four times fewer tiles run
+// back to back per wave.
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
@@ -540,7 +541,7 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
     constexpr int DS = D / 2;
     constexpr int LD = D + 1;        // padded row stride (floats)
     constexpr int WTILE = 2 * BC * LD;   // one wave's K and V tile (floats)
-    static_assert(WAVES * WTILE >= WAVES * QPW * D + 2 * WAVES * QPW, "merge area fits the tiles");
+    static_assert(WAVES * WTILE >= WAVES * QPW * D + 3 * WAVES * QPW, "merge area fits the tiles");
     __shared__ float lds[WAVES * WTILE];
 
     const int tid = threadIdx.x;
@@ -675,23 +676,32 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
         ml[wave * QPW + l32] = lt;
     }
     __syncthreads();
-    for (int idx = tid; idx < QPW * D; idx += NT) {
-        const int r = idx / D, col = idx % D;
+    // per row: M, l, one reciprocal, and the weight 2^(m_w - M) / l of each wave's O
+    float* mwt = ml + WAVES * QPW;                    // [WAVES][QPW] weights
+    if (tid < QPW) {
+        const int r = tid;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mm[w * QPW + r]);
-        float l = 0.f, acc = 0.f;
+        float sc[WAVES], l = 0.f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
             const float mw = mm[w * QPW + r];
-            const float sc = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-            l += sc * ml[w * QPW + r];
-            acc += sc * mo[(w * QPW + r) * D + col];
+            sc[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            l += sc[w] * ml[w * QPW + r];
         }
-        if (q0 + r < N) {
-            Oh[(int64_t)(q0 + r) * D + col] = acc / l;
-            if (col == 0) Lh[q0 + r] = (M + __builtin_amdgcn_logf(l)) * kLn2;
-        }
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) mwt[w * QPW + r] = sc[w] * inv;
+        if (q0 + r < N) Lh[q0 + r] = (M + __builtin_amdgcn_logf(l)) * kLn2;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < QPW * D; idx += NT) {
+        const int r = idx / D, col = idx % D;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) acc += mwt[w * QPW + r] * mo[(w * QPW + r) * D + col];
+        if (q0 + r < N) Oh[(int64_t)(q0 + r) * D + col] = acc;
     }
 }
 
@@ -726,9 +736,8 @@ static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int cau
 
 }  // namespace fa
 
-int fa_launch_fwd_splitkv(const fa::FwdArgs& a, int64_t rows, int dtype, int d, void* stream) {
+int fa_launch_fwd_splitkv(const fa::FwdArgs& a, int64_t rows, int dtype, int d, hipStream_t st) {
     using namespace fa;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == FA_BF16)
         e = d == 128 ? launch_splitkv_t<__bf16, 128, 64>(a, rows, st) : launch_splitkv_t<__bf16, 64, 128>(a, rows, st);
@@ -737,9 +746,8 @@ int fa_launch_fwd_splitkv(const fa::FwdArgs& a, int64_t rows, int dtype, int d, 
     return (int)e;
 }
 
-int fa_launch_fwd(const fa::FwdArgs& a, const fa_plan& plan, int dtype, int d, int causal, void* stream) {
+int fa_launch_fwd(const fa::FwdArgs& a, const fa_plan& plan, int dtype, int d, int causal, hipStream_t st) {
     using namespace fa;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == FA_BF16) {
         e = launch_half<__bf16>(a, plan, d, causal, st);

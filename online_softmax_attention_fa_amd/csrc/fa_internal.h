@@ -252,9 +252,9 @@ inline bool apply_tile_override(fa_plan* p, const char* tile, int64_t B, int64_t
 // Launchers implemented in fa_fwd_kernel.hip.  Return 0 on success or the
 // hipError_t of the launch.
 int fa_launch_fwd(const fa::FwdArgs& a, const fa_plan& plan, int dtype, int d, int causal,
-                  void* stream);
+                  hipStream_t stream);
 // Split-KV forward (bf16/fp16, non-causal): a.splits > 1, a.o_part / a.lse_part set;
 // launches the partial kernel and the merge.  rows = B*H*N.
-int fa_launch_fwd_splitkv(const fa::FwdArgs& a, int64_t rows, int dtype, int d, void* stream);
+int fa_launch_fwd_splitkv(const fa::FwdArgs& a, int64_t rows, int dtype, int d, hipStream_t stream);
 // rows = B*H*N.  Launches the preprocess, dQ and dK/dV kernels in stream order.
-int fa_launch_bwd(const fa::BwdArgs& a, int64_t rows, int dtype, int d, int causal, void* stream);
+int fa_launch_bwd(const fa::BwdArgs& a, int64_t rows, int dtype, int d, int causal, hipStream_t stream);
