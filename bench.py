@@ -28,13 +28,16 @@ ONE JSON line on stdout (everything else goes to stderr):
              kernel is power-bound on this workload, so these numbers bound its rate
   configs    forward time of the four other workloads at their real sizes: fp32 B1 H1 N256
              d64 (latency-bound), bf16 B4 H16 N2048 d64, fp16 B1 H32 N16384 d128 and the edge
-             workload bf16 B2 H8 N4097 d128 (zero, x10 and one-hot heads); median and min of
-             per-launch events, TFLOP/s and % of the MFMA peak of the input type
+             workload bf16 B2 H8 N4097 d128 (zero, x10 and one-hot heads), each after 0.2 s
+             of warm-up launches: the mean of 50 launches queued back to back (TFLOP/s and
+             % of the MFMA peak of the input type are taken from it), and the median and min
+             of per-launch events, whose intervals also hold each event's own gap
   causal     the causal forward (fa_fwd_causal) on the same tensors, TFLOP/s counted on the
              computed half (2*B*H*N^2*d)
   hbm_small_n  short sequences at B*H = 1024, d = 128, bf16, N in {128, 256, 512}, where the
              forward is bounded by HBM: algorithmic bytes (Q, K, V read once, O and LSE
-             written once) per launch time, as GB/s and % of the 8 TB/s HBM peak
+             written once) per launch (back-to-back mean, as for configs), as GB/s and % of
+             the 8 TB/s HBM peak
   sweep      (--sweep only) forward time of the smaller workloads (fp32 B1 H1 N256 d64,
              bf16 B4 H16 N2048 d64, fp16 B1 H32 N16384 d128, bf16 B2 H8 N4097 d128), the
              causal and split-KV variants, the fp8 forward causal at d=128 and at d=64,
@@ -345,16 +348,33 @@ def launch_times(fn, stream, steps, warmup=5, warm_seconds=0.2):
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
 
+def back_to_back_ms(fn, stream, n):
+    """Mean time (ms) of n launches queued back to back between two events, nothing between
+    them: the rate of a stream of calls, without the per-launch event records."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def _timed_case(fa, stream, q, k, v, scale, steps):
+    """(min, median) per-launch ms, back-to-back mean ms over 50 launches, outputs finite."""
     import statistics
 
     import torch
 
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], device=q.device, dtype=torch.float32)
-    t = launch_times(lambda: fa.fa_fwd(q, k, v, o, lse, scale=scale, stream=stream), stream, steps)
+    fn = lambda: fa.fa_fwd(q, k, v, o, lse, scale=scale, stream=stream)
+    t = launch_times(fn, stream, steps)
+    mean = back_to_back_ms(fn, stream, 50)
     ok = bool(torch.isfinite(o).all().item() and torch.isfinite(lse).all().item())
-    return min(t), statistics.median(t), ok
+    return min(t), statistics.median(t), mean, ok
 
 
 def _upload(x, dtype, dev):
@@ -391,19 +411,19 @@ def configs_leg(fa, stream, steps=20):
         else:
             q, k, v = (torch.randn(w.B, w.H, w.N, w.d, device=dev, dtype=dt, generator=gen) for _ in range(3))
             source = "device N(0,1), torch Philox"
-        tmin, tmed, ok = _timed_case(fa, stream, q, k, v, w.scale, steps)
+        tmin, tmed, tmean, ok = _timed_case(fa, stream, q, k, v, w.scale, steps)
         peak = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
-        tf = w.flops / (tmed * 1e-3) / 1e12
+        tf = w.flops / (tmean * 1e-3) / 1e12
         nbytes = 4.0 * w.B * w.H * w.N * w.d * q.element_size() + 4.0 * w.B * w.H * w.N
         r = {"workload": f"{w.dtype} B{w.B} H{w.H} N{w.N} d{w.d}" + (" edge heads" if w.kind == "edge" else ""),
-             "median_us": round(1e3 * tmed, 2), "min_us": round(1e3 * tmin, 2), "tflops": round(tf, 2),
-             "pct_of_mfma_peak": round(100 * tf / peak, 2), "peak_tflops": peak,
-             "gbps_algorithmic": round(nbytes / (tmed * 1e-3) / 1e9, 1),
+             "mean_us": round(1e3 * tmean, 2), "median_us": round(1e3 * tmed, 2), "min_us": round(1e3 * tmin, 2),
+             "tflops": round(tf, 2), "pct_of_mfma_peak": round(100 * tf / peak, 2), "peak_tflops": peak,
+             "gbps_algorithmic": round(nbytes / (tmean * 1e-3) / 1e9, 1),
              "plan": fa.fa_fwd_plan(w.B, w.H, w.N, w.d, dt), "outputs_finite": ok, "inputs": source}
         if cid == 1:
             r["note"] = "latency-bound (8 workgroups): microseconds and GB/s, no roofline claim"
         rows.append(r)
-        log(f"config {r['workload']}: median {r['median_us']} us, {r['tflops']} TFLOP/s = "
+        log(f"config {r['workload']}: mean {r['mean_us']} us (per-launch median {r['median_us']}), {r['tflops']} TFLOP/s = "
             f"{r['pct_of_mfma_peak']}% of peak, finite={ok}")
         del q, k, v
     return rows
@@ -419,15 +439,16 @@ def hbm_small_n_leg(fa, stream, steps=20):
     rows = []
     for n in (128, 256, 512):
         q, k, v = (torch.randn(b, h, n, d, device=dev, dtype=torch.bfloat16, generator=gen) for _ in range(3))
-        tmin, tmed, ok = _timed_case(fa, stream, q, k, v, 1.0 / math.sqrt(d), steps)
+        tmin, tmed, tmean, ok = _timed_case(fa, stream, q, k, v, 1.0 / math.sqrt(d), steps)
         nbytes = 4.0 * b * h * n * d * 2 + 4.0 * b * h * n
-        gbps = nbytes / (tmed * 1e-3) / 1e9
-        rows.append({"workload": f"bf16 B{b} H{h} N{n} d{d}", "median_us": round(1e3 * tmed, 2),
-                     "min_us": round(1e3 * tmin, 2), "algorithmic_bytes": nbytes, "gbps": round(gbps, 1),
+        gbps = nbytes / (tmean * 1e-3) / 1e9
+        rows.append({"workload": f"bf16 B{b} H{h} N{n} d{d}", "mean_us": round(1e3 * tmean, 2),
+                     "median_us": round(1e3 * tmed, 2), "min_us": round(1e3 * tmin, 2),
+                     "algorithmic_bytes": nbytes, "gbps": round(gbps, 1),
                      "pct_of_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
                      "flop_per_byte": round(4.0 * b * h * n * n * d / nbytes, 1),
                      "plan": fa.fa_fwd_plan(b, h, n, d, torch.bfloat16), "outputs_finite": ok})
-        log(f"hbm small N={n}: median {rows[-1]['median_us']} us, {rows[-1]['gbps']} GB/s = "
+        log(f"hbm small N={n}: mean {rows[-1]['mean_us']} us (per-launch median {rows[-1]['median_us']}), {rows[-1]['gbps']} GB/s = "
             f"{rows[-1]['pct_of_hbm_peak']}% of 8 TB/s")
         del q, k, v
     return rows
