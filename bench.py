@@ -23,6 +23,9 @@ ONE JSON line on stdout (everything else goes to stderr):
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload (whole heads
              in row chunks, all keys, about 15 s of host time), timed on the host
              cores, with the GPU output checked on the same rows
+  mfma_busy  the forward's MFMA-busy fraction (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES per SIMD cycle)
+             and clock from the committed counter summary, when it was taken on the current
+             kernel source, else null
   power      socket power and GFX clock (amd-smi) sampled while the forward runs back to back
              for --power-seconds after the timed steps, with the board's power cap; the
              kernel is power-bound on this workload, so these numbers bound its rate
@@ -102,6 +105,24 @@ def traffic_from_profile():
     if m_hash.group(1) != kernel_source_hash():
         return None, "kernel changed since counters were taken"
     return float(m_bytes.group(1)), "ok"
+
+
+def mfma_busy_from_profile():
+    """The forward's MFMA-busy fraction and clock from the committed counter summary
+    (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE / 8), if it matches this
+    source: the share of the matrix cores' cycles the kernel keeps them working, the peak
+    fraction at the clock the chip actually ran."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    m_busy = re.search(r"\| MFMA busy per SIMD \| ([0-9.]+) %", text)
+    m_clk = re.search(r"MFMA peak at ([0-9.]+) GHz", text)
+    if not (m_hash and m_busy and m_clk) or m_hash.group(1) != kernel_source_hash():
+        return None
+    return {"frac": round(float(m_busy.group(1)) / 100, 4), "clock_ghz": float(m_clk.group(1)),
+            "source": "profiles/fa_fwd_bf16_B4_H32_N16384_d128_counters.md: SQ_VALU_MFMA_BUSY_CYCLES / "
+                      "(1024 SIMDs x GRBM_GUI_ACTIVE / 8), rocprofv3 counter run of this kernel source"}
 
 
 def cpu_baseline(q, k, v, o, lse, scale, budget_s=15.0, chunk=2048):
@@ -664,6 +685,7 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
         },
+        "mfma_busy": mfma_busy_from_profile(),
     }
     # the shorter legs run first, before the sustained power, backward and fp8 legs heat the chip
     if not args.no_configs:
