@@ -538,3 +538,47 @@ def test_huge_sizes_are_rejected_without_overflow(lib):
     assert _f8(lib, N=big) == 2
     plan = fa.Plan()
     assert lib.fa_fwd_plan(big, big, big, 128, fa.FA_BF16, 0, ctypes.byref(plan)) == 2
+
+
+def test_header_builds_as_c_and_links(tmp_path):
+    # A plain C11 caller: includes fa.h alone (it declares hipStream_t itself), links
+    # libfa.so and calls the host-only entry points.
+    import subprocess
+
+    src = tmp_path / "caller.c"
+    src.write_text(
+        '#include "fa.h"\n#include <stdio.h>\n'
+        "int main(void) {\n"
+        "    fa_plan p;\n"
+        "    hipStream_t s = 0;\n"
+        "    (void)s;\n"
+        "    if (fa_fwd_plan(4, 32, 16384, 128, FA_BF16, 0, &p) != FA_OK) return 1;\n"
+        '    printf("%d %d %d %d\\n", fa_version() >= 100, p.block_q, p.block_k, p.waves);\n'
+        "    return 0;\n}\n")
+    exe = tmp_path / "caller"
+    lib = os.path.join(os.path.dirname(os.path.abspath(fa.__file__)), "libfa.so")   # the in-tree build
+    if not os.path.exists(lib):
+        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    # the children run without the sanitizer runtime a parent run may preload
+    env = {k: v for k, v in os.environ.items() if not k.startswith(("LD_PRELOAD", "ASAN_", "UBSAN_"))}
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    lib, f"-Wl,-rpath,{os.path.dirname(lib)}"], check=True, capture_output=True, text=True, env=env)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, env=env).stdout.split()
+    assert out == ["1", "256", "128", "8"]
+
+
+def test_header_typedef_agrees_with_hip():
+    # C++ callers that include HIP's runtime header first see the same hipStream_t.
+    import subprocess
+
+    hip_inc = "/opt/rocm/include"
+    if not os.path.exists(os.path.join(hip_inc, "hip", "hip_runtime_api.h")):
+        pytest.skip("HIP headers not installed")
+    code = ('#include <hip/hip_runtime_api.h>\n#include "fa.h"\n'
+            "static_assert(sizeof(hipStream_t) == sizeof(void*), \"handle\");\n"
+            "int f(hipStream_t s) { return fa_fwd(0, 0, 0, 0, 0, 0, 0, 0, 64, 1.0f, FA_BF16, s); }\n")
+    env = {k: v for k, v in os.environ.items() if not k.startswith(("LD_PRELOAD", "ASAN_", "UBSAN_"))}
+    r = subprocess.run(["g++", "-std=c++17", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__", "-I", hip_inc,
+                        "-I", os.path.join(ROOT, "include"), "-x", "c++", "-"], input=code, capture_output=True,
+                       text=True, env=env)
+    assert r.returncode == 0, r.stderr
