@@ -42,10 +42,11 @@ struct Fp8Args {
     int n_blocks;
     float c;                   // scale * log2(e)
 };
-// Query rows per workgroup of the fp8 forward: 4 waves x 32 rows, two workgroups per CU.
-// (Measured at B=4 H=32 N=16384 d=128: 8% faster than one 8-wave workgroup per CU; the
-// two independent workgroups on a CU drift out of phase, so one's softmax overlaps the
-// other's MFMAs, where the waves of one workgroup meet at every tile's barrier.)
+// Query rows per workgroup of the fp8 forward: 4 waves x 32 rows, three workgroups per CU
+// (64-key tiles: 32 KiB of LDS, at most 168 VGPRs).  Measured at B=4 H=32 N=16384 d=128: two
+// 4-wave workgroups per CU were 8% faster than one 8-wave workgroup (independent workgroups
+// drift out of phase, so one's softmax overlaps another's MFMAs, where the waves of one
+// workgroup meet at every tile's barrier), and a third per CU another 8%.
 constexpr int kFp8BlockQ = 128;
 
 }  // namespace fa
