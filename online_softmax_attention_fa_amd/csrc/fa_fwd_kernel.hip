@@ -167,6 +167,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         const int ch = ((off % RB) >> 4) ^ swz<CPR>(row);
         src_off[i] = row * RB + ch * 16;
     }
+    // s_waitcnt immediate for vmcnt(2 LOADS) -- one tile's K and V copies still in flight --
+    // in the gfx9 encoding (vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left unwaited)
+    constexpr int kTileLoads = 2 * LOADS;
+    static_assert(kTileLoads < 64, "vmcnt is six bits");
+    constexpr unsigned kWaitOneTileInFlight = 0x0F70u | (kTileLoads & 15) | ((kTileLoads >> 4) << 14);
     auto issue_tile = [&](int j, lds_u8* stage) {
         const int soff = j * BC * RB;
 #if defined(FA_LDS_POISON)
@@ -381,20 +386,38 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
             pp_step(j + 2, stage2);
         }
     } else {
-        if (t0 < n_tiles) issue_tile(t0, stage0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's LDS copies have landed
-        __syncthreads();
-
-        for (int j = t0; j < n_tiles; j += 2) {
-            // stage 0 holds tile j; tile j + 1 streams into stage 1 meanwhile
-            if (j + 1 < n_tiles) issue_tile(j + 1, stage1);
-            if (has_rows && (!CAUSAL || j * BC <= q_wave + QPW - 1)) compute_tile(j, stage0);
+        // The first tile is computed ahead of the loop with the second tile's copy already in
+        // flight: both are issued together and the wait covers only the first (vector-memory
+        // loads complete in order), so the second copy overlaps the first one's wait as well
+        // as its compute.  Heads of a few tiles are bound by these copy latencies.
+        auto computes = [&](int j) { return has_rows && (!CAUSAL || j * BC <= q_wave + QPW - 1); };
+        if (t0 < n_tiles) {
+            issue_tile(t0, stage0);
+            if (t0 + 1 < n_tiles) {
+                issue_tile(t0 + 1, stage1);
+                // No release fence before this barrier: it would wait for the second tile's
+                // copies too, which no wave reads before the next full barrier.
+                __builtin_amdgcn_s_waitcnt(kWaitOneTileInFlight);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's LDS copies have landed
+                __syncthreads();
+            }
+            if (computes(t0)) compute_tile(t0, stage0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);       // the second tile has landed
+            __syncthreads();
+        }
+        for (int j = t0 + 1; j < n_tiles; j += 2) {
+            // stage 1 holds tile j; tile j + 1 streams into stage 0 meanwhile
+            if (j + 1 < n_tiles) issue_tile(j + 1, stage0);
+            if (computes(j)) compute_tile(j, stage1);
             __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
             if (j + 1 >= n_tiles) break;
-            // stage 1 holds tile j + 1
-            if (j + 2 < n_tiles) issue_tile(j + 2, stage0);
-            if (has_rows && (!CAUSAL || (j + 1) * BC <= q_wave + QPW - 1)) compute_tile(j + 1, stage1);
+            // stage 0 holds tile j + 1
+            if (j + 2 < n_tiles) issue_tile(j + 2, stage1);
+            if (computes(j + 1)) compute_tile(j + 1, stage0);
             __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
         }
