@@ -110,6 +110,8 @@ typedef struct {
     int32_t kv_splits;      /* >1: key range split across workgroups, then merged      */
     int32_t wave_kv_splits; /* >1: a workgroup's waves share its query rows and split  */
                             /*     the key tiles among themselves, merged in LDS       */
+    int32_t tail_kv_splits; /* >1: the same for the last query block of each head only */
+                            /*     (at most 32 rows; whole grid resident at once)      */
 } fa_plan;
 
 /*

@@ -48,7 +48,7 @@ class Plan(ctypes.Structure):
     _fields_ = [
         ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("waves", ctypes.c_int32),
         ("rows_per_wave", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("grid", ctypes.c_int64),
-        ("kv_splits", ctypes.c_int32), ("wave_kv_splits", ctypes.c_int32),
+        ("kv_splits", ctypes.c_int32), ("wave_kv_splits", ctypes.c_int32), ("tail_kv_splits", ctypes.c_int32),
     ]
 
     def as_dict(self):

@@ -85,7 +85,9 @@ fa_status make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int c
     *plan = fa::choose_fwd_plan(B, H, N, d, dtype, causal);
     const char* tile = getenv("FA_TILE");
     *overridden = tile && *tile;
-    return fa::apply_tile_override(plan, tile, B, H, N, d, dtype, causal) ? FA_OK : FA_ERR_TILE;
+    if (!fa::apply_tile_override(plan, tile, B, H, N, d, dtype, causal)) return FA_ERR_TILE;
+    plan->tail_kv_splits = fa::fwd_tail_kv_splits(*plan, dtype, N, N, d, causal);
+    return FA_OK;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -121,11 +123,14 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
     st = make_plan(B, H, N, d, dtype, causal, &plan, &overridden);
     if (st != FA_OK) return st;
     if (plan.grid >= kMaxGrid) return FA_ERR_SHAPE;
+    plan.tail_kv_splits = fa::fwd_tail_kv_splits(plan, dtype, N, Nk, d, causal);
     if (log_enabled())
-        fprintf(stderr, "fa_fwd%s: B=%lld H=%lld N=%lld Nk=%lld d=%lld %s -> Br=%d Bc=%d waves=%d grid=%lld lds=%d%s%s\n",
+        fprintf(stderr, "fa_fwd%s: B=%lld H=%lld N=%lld Nk=%lld d=%lld %s -> Br=%d Bc=%d waves=%d grid=%lld lds=%d%s%s%s\n",
                 causal ? "_causal" : "", (long long)B, (long long)H, (long long)N, (long long)Nk, (long long)d,
                 dtype_name(dtype), plan.block_q, plan.block_k, plan.waves, (long long)plan.grid, plan.lds_bytes,
-                plan.wave_kv_splits > 1 ? " (waves split the key tiles)" : "", overridden ? " (FA_TILE)" : "");
+                plan.wave_kv_splits > 1 ? " (waves split the key tiles)" : "",
+                plan.tail_kv_splits > 1 ? " (the last block's waves split the key tiles)" : "",
+                overridden ? " (FA_TILE)" : "");
     st = check_device();
     if (st != FA_OK) return st;
 

@@ -60,7 +60,7 @@ namespace fa {
 // so if lane r of the group addresses V[k0 + r/4][d0 + 4(r%4) .. +3], lane c gets
 // V[k0 + e][d0 + c] for e = 0..3: four keys of its own column.
 
-template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool SPLIT = false, bool PP = false>
+template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool SPLIT = false, bool PP = false, bool TAIL = false>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 2) : 1) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource types exist only in the device pass
     constexpr int NT = 64 * WAVES, QPW = 32, BR = WAVES * QPW;
@@ -79,6 +79,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     static_assert(LOADS >= 1 && TILE % (NT * 16) == 0, "tile must be whole 4 KiB blocks");
     static_assert(!(SPLIT && CAUSAL), "split-KV is non-causal");
     static_assert(!PP || (WAVES == 8 && !CAUSAL && !SPLIT), "ping-pong: 8 waves, non-causal");
+    static_assert(!TAIL || (WAVES == 4 && !CAUSAL && !SPLIT), "last-block key split: 4 waves, non-causal");
 
     // Two stages in two separate arrays: the compiler can then prove that the copies
     // into one stage do not alias the reads of the other and adds no wait for them.
@@ -116,7 +117,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     T* __restrict__ Oh = reinterpret_cast<T*>(a.o) + head;
     float* __restrict__ Lh = a.lse + (int64_t)bh * N;
 
-    const int q_wave = qblk * BR + wave * QPW;   // first query row of this wave
+    // TAIL: a block whose rows all fit in its first wave (the one-row last block when N is one
+    // more than a multiple of Br; one-query decoding) would leave its other waves idle while
+    // the first sweeps every key.  There every wave takes the first wave's rows and a quarter
+    // of the key tiles, and the four partial results are merged through LDS at the end.  A
+    // variant of its own, launched where it measured faster, so the others keep their code.
+    constexpr bool kTailSplit = TAIL;
+    const bool tail_split = kTailSplit && N - qblk * BR <= QPW;
+    const int q_wave = qblk * BR + (tail_split ? 0 : wave * QPW);   // first query row of this wave
     const int query = q_wave + l32;              // the query this lane's columns belong to
     // A wave whose 32 rows all lie past N (the last query block; one-query decoding) skips
     // the tile work, not the copies or barriers: its rows are never stored.
@@ -213,8 +221,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     }
 
     u32x4 pf[KS];   // P of the current tile, packed: the B operand of O^T += V^T P^T
-    // S, the masks, P and the row sums of tile j
-    auto qk_soft = [&](int j, const lds_u8* sbase) __attribute__((always_inline)) {
+    // S, the masks, P and the row sums of tile j; kread(i) gives the K fragment of k-step i
+    auto qk_soft_with = [&](int j, auto kread, int jfirst) __attribute__((always_inline)) {
         const int kbase = j * BC;
         // MFMA-heavy stretches run at raised wave priority, so the SIMD issues them ahead of
         // the other wave's VALU work (measured 0.4-3% faster in every variant).
@@ -233,20 +241,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         constexpr int NQK = KB * DS, KPF = 6;
         u32x4 kf[KPF + 1];
 #pragma unroll
-        for (int i = 0; i < KPF; ++i) kf[i] = lds_read16(sbase, koff[i % DS] + (i / DS) * 32 * RB);
+        for (int i = 0; i < KPF; ++i) kf[i] = kread(i);
 #pragma unroll
         for (int i = 0; i < NQK; ++i) {
-            if (i + KPF < NQK)
-                kf[(i + KPF) % (KPF + 1)] = lds_read16(sbase, koff[(i + KPF) % DS] + ((i + KPF) / DS) * 32 * RB);
+            if (i + KPF < NQK) kf[(i + KPF) % (KPF + 1)] = kread(i + KPF);
             s[i / DS] = Elt<T>::mma(kf[i % (KPF + 1)], qf[i % DS], s[i / DS]);
             __builtin_amdgcn_sched_barrier(0);
         }
 
         __builtin_amdgcn_s_setprio(0);
         // ---- masks: keys past NK (tail tile), keys after the query (causal)
-        const bool tail = kbase + BC > NK;
+        const bool ragged = kbase + BC > NK;
         const bool diag = CAUSAL && (kbase + BC - 1 > q_wave);
-        if (tail || diag) {
+        if (ragged || diag) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         // The workgroup's first tile meets m = -inf, which would fail the test anyway: it takes
         // its own maximum at once.  (NaN, from -inf scores against m = -inf, fails the test.)
         bool redo = true;
-        if (j != t0) {
+        if (j != jfirst) {
             make_p(-m);
             redo = __builtin_amdgcn_ballot_w64(!((ONE_SUM ? racc0 + racc1 : acc0 + acc1) <= kMaxTileSum)) != 0;
         }
@@ -319,8 +326,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         if constexpr (!ONE_SUM) lsum += acc0 + acc1;
         lrnd += racc0 + racc1;
     };
-    // O^T += V_j^T P^T
-    auto pv = [&](const lds_u8* sbase) __attribute__((always_inline)) {
+    auto qk_soft = [&](int j, const lds_u8* sbase) __attribute__((always_inline)) {
+        qk_soft_with(j, [&](int i) { return lds_read16(sbase, koff[i % DS] + (i / DS) * 32 * RB); }, t0);
+    };
+    // O^T += V_j^T P^T; vo(aa, db) gives the lane's LDS offsets of V_j from sbase
+    auto pv_from = [&](const lds_u8* sbase, auto vo) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
         // (same order: the KS k-steps of one 32-dim block of O^T back to back, V^T fragments
         // gathered VPF steps ahead)
@@ -328,8 +338,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
             constexpr int NPV = KS * DB, VPF = 4;
             auto vread = [&](int i) {
                 const int db = i / KS, ks = i % KS;
-                const u32x2 lo = lds_read_tr(sbase, voff[0][db] + ks * 16 * RB);
-                const u32x2 hi = lds_read_tr(sbase, voff[1][db] + ks * 16 * RB);
+                const u32x2 lo = lds_read_tr(sbase, vo(0, db) + ks * 16 * RB);
+                const u32x2 hi = lds_read_tr(sbase, vo(1, db) + ks * 16 * RB);
                 return u32x4{lo[0], lo[1], hi[0], hi[1]};
             };
             u32x4 vf[VPF + 1];
@@ -343,6 +353,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
             }
         }
         __builtin_amdgcn_s_setprio(0);
+    };
+    auto pv = [&](const lds_u8* sbase) __attribute__((always_inline)) {
+        pv_from(sbase, [&](int aa, int db) { return voff[aa][db]; });
     };
     auto compute_tile = [&](int j, const lds_u8* sbase) __attribute__((always_inline)) {
         qk_soft(j, sbase);
@@ -371,7 +384,104 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
             __syncthreads();
         }
     };
-    if constexpr (PP) {
+    if (tail_split) {
+        if constexpr (kTailSplit) {
+            // Wave w takes key tiles [tb, te).  Its V tiles go HBM -> LDS into a region of its
+            // own (one tile; the two stages hold four) and its K fragments straight into
+            // registers, read as the score MFMAs consume them (through the same prefetch window
+            // as the LDS reads of the other blocks), so the waves meet only at the merge.
+            const int per = (n_tiles + WAVES - 1) / WAVES;
+            const int tb = min(n_tiles, wave * per), te = min(n_tiles, tb + per);
+            lds_u8* const region = (wave < 2 ? stage0 : stage1) + (wave & 1) * TILE;
+            constexpr int VLOADS = TILE / 1024;   // 1 KiB copies per V tile
+            auto issue_v = [&](int j) {   // row-major V tile, swizzled as in issue_tile
+#if defined(FA_LDS_POISON)
+#pragma unroll
+                for (int i = 0; i < VLOADS; ++i)
+                    *reinterpret_cast<lds_u32x4*>(region + i * 1024 + lane * 16) = u32x4{~0u, ~0u, ~0u, ~0u};
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+#endif
+#pragma unroll
+                for (int i = 0; i < VLOADS; ++i) {
+                    const int off = i * 1024 + lane * 16;
+                    const int row = off / RB;
+                    const int ch = ((off % RB) >> 4) ^ swz<CPR>(row);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(region + i * 1024), 16,
+                                                             j * BC * RB + row * RB + ch * 16, 0, 0, 0);
+                }
+            };
+            // V offsets in the region, recomputed here from the hardware lane id (as a value the
+            // compiler cannot equate with the one before the branch, so no input of this path
+            // stays live across the other path's loop)
+            const int tl = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+            int tvoff[2][DB];
+            {
+                const int g = tl >> 4, r = tl & 15, th = tl >> 5;
+#pragma unroll
+                for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const int key = 8 * aa + 4 * th + (r >> 2);
+                        const int dim = 32 * db + 16 * (g & 1) + 4 * (r & 3);
+                        tvoff[aa][db] = key * RB + 16 * ((dim >> 3) ^ swz<CPR>(key)) + 2 * (dim & 7);
+                    }
+            }
+            if (tb < te) issue_v(tb);
+            for (int j = tb; j < te; ++j) {
+                // k-step i: keys j Bc + 32 (i / DS) + l32, dims 16 (i % DS) + 8 h .. + 7 -- the
+                // fragment the LDS reads deliver
+                qk_soft_with(j, [&](int i) {
+                    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        krs, (j * BC + (i / DS) * 32 + l32) * RB + ((i % DS) * 16 + h * 8) * 2, 0, 0));
+                }, tb);
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this tile's V has landed
+                pv_from(region, [&](int aa, int db) { return tvoff[aa][db]; });
+                if (j + 1 < te) {
+                    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the V reads are done
+                    issue_v(j + 1);
+                }
+            }
+            // Merge into wave 0, one partial at a time: O^T through stage 0 and the row
+            // statistics through tail_stats, both in the accumulator layout, so each lane of
+            // wave 0 combines the entries of the same lane of wave w.
+            __shared__ float tail_stats[3 * 64];
+            typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+            lds_f32x4* const opart = (lds_f32x4*)stage0;
+            static_assert(DB * 4 * 64 * 16 <= STAGE, "a wave's O^T fits in one stage");
+#pragma unroll 1
+            for (int w = 1; w < WAVES; ++w) {
+                __syncthreads();
+                if (wave == w) {
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            opart[(db * 4 + g) * 64 + lane] =
+                                f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+                    tail_stats[lane] = m;
+                    tail_stats[64 + lane] = lsum;
+                    tail_stats[128 + lane] = lrnd;
+                }
+                __syncthreads();
+                const float mw = tail_stats[lane];
+                if (wave == 0 && mw != -INFINITY) {   // a wave without key tiles adds nothing
+                    const float mn = fmaxf(m, mw);
+                    const float a0 = fast_exp2(m - mn), aw = fast_exp2(mw - mn);
+                    m = mn;
+                    lsum = lsum * a0 + tail_stats[64 + lane] * aw;
+                    lrnd = lrnd * a0 + tail_stats[128 + lane] * aw;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const f32x4 x = opart[(db * 4 + g) * 64 + lane];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) o[db][4 * g + e] = o[db][4 * g + e] * a0 + x[e] * aw;
+                        }
+                }
+            }
+        }
+    } else if constexpr (PP) {
         if (t0 < n_tiles) issue_tile(t0, stage0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
@@ -451,7 +561,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     // of 32 rows.  The stages are free once every wave has passed this barrier (in the
     // ping-pong schedule the late group's last P V reads a stage after its last tile barrier).
     __syncthreads();
-    if (has_rows) {
+    if (has_rows && (!tail_split || wave == 0)) {
         constexpr int WPS = BC / 16;               // waves whose 32 rows fit in one stage
         lds_u8* obuf = (wave / WPS == 0 ? stage0 : stage1) + (wave % WPS) * (QPW * RB);
         // Staging layout: 16-byte chunk c of row r sits in slot c ^ ochunk(r) and its two
@@ -730,30 +840,38 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
 
 // ------------------------------------------------------------------ dispatch ---
 
+// tail: the plan's last-block key split (non-causal 4-wave plans only)
 template <typename T, int D, int BC, int WAVES>
-static hipError_t launch_t(const FwdArgs& a, int causal, hipStream_t st) {
+static hipError_t launch_t(const FwdArgs& a, int causal, bool tail, hipStream_t st) {
     const dim3 grid((unsigned)a.n_blocks), block(64 * WAVES);
-    if (causal)
+    if (causal) {
         hipLaunchKernelGGL((fwd_kernel<T, D, BC, WAVES, true>), grid, block, 0, st, a);
-    else
+    } else if (tail) {
+        if constexpr (WAVES == 4)
+            hipLaunchKernelGGL((fwd_kernel<T, D, BC, WAVES, false, false, false, true>), grid, block, 0, st, a);
+        else
+            return hipErrorInvalidConfiguration;
+    } else {
         hipLaunchKernelGGL((fwd_kernel<T, D, BC, WAVES, false>), grid, block, 0, st, a);
+    }
     return hipGetLastError();
 }
 
 // The compiled (d, Bc, waves) shapes; the chooser only emits these.
 template <typename T>
 static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int causal, hipStream_t st) {
-    if (d == 128 && p.block_k == 128 && p.waves == 8) return launch_t<T, 128, 128, 8>(a, causal, st);
+    const bool tail = p.tail_kv_splits > 1;
+    if (d == 128 && p.block_k == 128 && p.waves == 8) return launch_t<T, 128, 128, 8>(a, causal, tail, st);
     if (d == 64 && p.block_k == 128 && p.waves == 8) {
-        if (causal) return launch_t<T, 64, 128, 8>(a, causal, st);
+        if (causal) return launch_t<T, 64, 128, 8>(a, causal, false, st);
         // non-causal d = 64 on the ping-pong schedule
         hipLaunchKernelGGL((fwd_kernel<T, 64, 128, 8, false, false, true>), dim3((unsigned)a.n_blocks), dim3(512), 0, st, a);
         return hipGetLastError();
     }
-    if (d == 128 && p.block_k == 64 && p.waves == 4) return launch_t<T, 128, 64, 4>(a, causal, st);
-    if (d == 64 && p.block_k == 128 && p.waves == 4) return launch_t<T, 64, 128, 4>(a, causal, st);
-    if (d == 64 && p.block_k == 64 && p.waves == 4) return launch_t<T, 64, 64, 4>(a, causal, st);
-    if (d == 128 && p.block_k == 32 && p.waves == 4) return launch_t<T, 128, 32, 4>(a, causal, st);
+    if (d == 128 && p.block_k == 64 && p.waves == 4) return launch_t<T, 128, 64, 4>(a, causal, tail, st);
+    if (d == 64 && p.block_k == 128 && p.waves == 4) return launch_t<T, 64, 128, 4>(a, causal, tail, st);
+    if (d == 64 && p.block_k == 64 && p.waves == 4) return launch_t<T, 64, 64, 4>(a, causal, tail, st);
+    if (d == 128 && p.block_k == 32 && p.waves == 4) return launch_t<T, 128, 32, 4>(a, causal, tail, st);
     return hipErrorInvalidConfiguration;
 }
 

@@ -166,6 +166,28 @@ def test_plan_respects_lds_and_covers_rows(lib, dtype, d):
         assert p["kv_splits"] >= 1
 
 
+def test_plan_splits_the_keys_of_a_short_last_block_only_on_grids_resident_at_once(lib):
+    # The last query block's waves share its <= 32 rows and split the key tiles four ways on
+    # non-causal 4-wave plans whose grid fits in one round, with at least 32 key tiles.
+    def tail(B, H, N, d, dtype=fa.FA_BF16, causal=False):
+        return fa.fa_fwd_plan(B, H, N, d, dtype, causal=causal)["tail_kv_splits"]
+
+    assert tail(2, 8, 4097, 128) == 4            # 528 workgroups at three per CU: one round
+    assert tail(2, 8, 4097, 128, fa.FA_F16) == 4
+    assert tail(2, 8, 4128, 128) == 4            # 32 rows in the last block
+    assert tail(2, 8, 4097, 64) == 4             # 64-key tiles at three per CU
+    assert tail(2, 4, 8193, 128) == 4
+    assert tail(2, 8, 4129, 128) == 1            # 33 rows: two waves hold rows
+    assert tail(4, 8, 4097, 128) == 1            # 1056 workgroups: more than one round
+    assert tail(2, 8, 4097, 128, causal=True) == 1
+    assert tail(1, 2, 257, 128) == 1             # 5 key tiles: too few to share
+    assert tail(4, 32, 16384, 128) == 1          # 8-wave plan, no ragged block
+    assert tail(1, 1, 4097, 64, fa.FA_F32) == 1
+    assert tail(0, 8, 4097, 128) == 0            # empty problem: the plan is all zeros
+    for B, H, N in [(1, 1, 1), (1, 1, 256), (4, 16, 2048), (2, 8, 4097), (4, 32, 16384)]:
+        assert fa.fa_fwd_plan(B, H, N, 128, fa.FA_BF16)["tail_kv_splits"] in (1, 4)
+
+
 def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_short_heads(lib):
     # 528 workgroups of 128 rows: two per CU leave a nearly empty second round, three per
     # CU (32-key tiles) fit them in one; causal grids and full rounds keep 64-key tiles

@@ -99,6 +99,45 @@ def test_causal(gpu_lib, dtype, d, N):
     compare(O, L, O_ref, L_ref, dtype, f"causal N={N} d={d} {dtype}")
 
 
+# ------------------------------------- one-wave last blocks: the keys split four ways ---
+
+# (FA_TILE, d): every non-causal 4-wave kernel
+TAIL_PLANS = [("128,32,4", 128), ("128,64,4", 128), ("128,64,4", 64), ("128,128,4", 64)]
+
+
+@pytest.mark.parametrize("tile,d", TAIL_PLANS, ids=[f"{t}-d{d}" for t, d in TAIL_PLANS])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("rows", [1, 17, 32])
+def test_one_wave_last_block(gpu_lib, monkeypatch, tile, d, dtype, rows):
+    # A last query block of `rows` <= 32 rows on a grid resident at once: its four waves all
+    # take those rows and a quarter of the key tiles each (34 to 38 tiles: the last wave
+    # holds fewer than the others), and merge through LDS.
+    monkeypatch.setenv("FA_TILE", tile)
+    bc = int(tile.split(",")[1])
+    N = 128 * (32 * bc // 128 + 1) + rows
+    plan = gpu_lib.fa_fwd_plan(1, 2, N, d, wl_dtype_code(dtype))
+    assert plan["tail_kv_splits"] == 4, plan
+    q, k, v = _random_qkv(1, 2, N, d, dtype, seed=N * 10 + d + rows)
+    O, L = run_fwd(gpu_lib, q, k, v, dtype)
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(d))
+    compare(O, L, O_ref, L_ref, dtype, f"FA_TILE={tile} d={d} {dtype} N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_one_wave_last_block_large_scores(gpu_lib, monkeypatch, dtype):
+    # Scores of several hundred: each wave's running maximum differs widely, so the merge
+    # rescales the partials by factors that underflow to zero for some rows.
+    monkeypatch.setenv("FA_TILE", "128,32,4")
+    N, d = 1281, 128
+    assert gpu_lib.fa_fwd_plan(1, 2, N, d, wl_dtype_code(dtype))["tail_kv_splits"] == 4
+    sigma = 10.0 if dtype == "bf16" else 4.0
+    q, k, v = _random_qkv(1, 2, N, d, dtype, seed=4242, sigma=sigma)
+    v = wl.random_tensor(v.shape, dtype, [4242, 9])
+    O, L = run_fwd(gpu_lib, q, k, v, dtype)
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(d))
+    compare(O, L, O_ref, L_ref, dtype, f"large scores N={N} {dtype}")
+
+
 # ------------------------------------------------------------ extreme inputs ---
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])

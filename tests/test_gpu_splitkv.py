@@ -109,6 +109,8 @@ def test_splitkv_long_single_head_sampled(gpu_lib):
     (1, 2, 7, 3000, 128, "fp16", 0),      # a few new queries against a long history
     (2, 2, 300, 100, 128, "bf16", 1),     # more queries than keys, no split
     (1, 2, 130, 4097, 64, "bf16", 9),
+    (2, 4, 1, 5000, 128, "bf16", 1),      # decode unsplit: the block's waves split the keys
+    (1, 2, 20, 3000, 64, "fp16", 1),
 ])
 def test_splitkv_unequal_lengths(gpu_lib, B, H, Nq, Nk, d, dtype, splits):
     import torch
