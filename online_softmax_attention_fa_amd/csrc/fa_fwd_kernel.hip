@@ -119,9 +119,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
 
     // TAIL: a block whose rows all fit in its first wave (the one-row last block when N is one
     // more than a multiple of Br; one-query decoding) would leave its other waves idle while
-    // the first sweeps every key.  There every wave takes the first wave's rows and a quarter
-    // of the key tiles, and the four partial results are merged through LDS at the end.  A
-    // variant of its own, launched where it measured faster, so the others keep their code.
+    // the first sweeps every key.  There every wave (four: the two stages hold four V tiles)
+    // takes the first wave's rows and a quarter of the key tiles, and the four partial results
+    // are merged through LDS at the end.  A variant of its own, launched where it measured
+    // faster, so the others keep their code.
     constexpr bool kTailSplit = TAIL;
     const bool tail_split = kTailSplit && N - qblk * BR <= QPW;
     const int q_wave = qblk * BR + (tail_split ? 0 : wave * QPW);   // first query row of this wave

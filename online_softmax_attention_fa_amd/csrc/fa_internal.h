@@ -209,7 +209,10 @@ inline int fwd_per_cu(int64_t d, int block_k, int waves) {
 // the whole grid is resident at once (B2 H8 N4097 d128 165 -> 148 us, B2 H4 N8193 321 -> 272
 // us, B2 H8 N4097 d64 105 -> 89 us), where the one busy wave of the last block holds up its
 // CU; 0.6-6.5% slower when the grid takes more than one round (B8 H16 N1025 79 -> 85 us),
-// and slower with few key tiles (each wave then waits out a copy latency per tile).
+// and slower with few key tiles (each wave then waits out a copy latency per tile).  On the
+// 8-wave plans (four of the eight waves splitting, the LDS holding four V tiles) it measured
+// within -6% and +2% of the plain kernel: with 128-key tiles each wave's K loads, six in
+// flight from a wave that runs alone, took about 5.6 us per tile.
 inline int fwd_tail_kv_splits(const fa_plan& p, int dtype, int64_t N, int64_t Nk, int64_t d, int causal) {
     if (dtype == FA_F32 || causal || p.waves != 4 || p.kv_splits > 1 || N <= 0) return 1;
     const int64_t last_rows = N - (ceil_div(N, p.block_q) - 1) * p.block_q;
