@@ -71,7 +71,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     constexpr int RB = D * 2;         // bytes per K/V row
     constexpr int CPR = D / 8;        // 16-byte chunks per row
     constexpr int TILE = BC * RB;     // bytes of one K (or V) tile
-    constexpr int STAGE = 2 * TILE;
     constexpr int LOADS = TILE / (NT * 16);   // direct loads per thread per tile, K or V
     // fp16: the fp16-rounded row sum serves O and the LSE alike (its relative error, at most
     // 2^-11 per term, moves the LSE by less than 1e-3); bf16 keeps an fp32 sum for the LSE
@@ -81,17 +80,40 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     static_assert(!PP || (WAVES == 8 && !CAUSAL && !SPLIT), "ping-pong: 8 waves, non-causal");
     static_assert(!TAIL || (WAVES == 4 && !CAUSAL && !SPLIT), "last-block key split: 4 waves, non-causal");
 
-    // Two stages in two separate arrays: the compiler can then prove that the copies
-    // into one stage do not alias the reads of the other and adds no wait for them.
-    __shared__ __attribute__((aligned(1024))) unsigned char stage0_raw[STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char stage1_raw[STAGE];
-    lds_u8* const stage0 = (lds_u8*)stage0_raw;
-    lds_u8* const stage1 = (lds_u8*)stage1_raw;
-    lds_u8* stage2 = nullptr;   // third stage of the ping-pong schedule
-    if constexpr (PP) {
-        __shared__ __attribute__((aligned(1024))) unsigned char stage2_raw[STAGE];
-        stage2 = (lds_u8*)stage2_raw;
+    // A stage is a K tile and a V tile.  Each stage is an array of its own, so the compiler
+    // can prove that the copies into one stage do not alias the reads of the other and adds no
+    // wait for them.  The 8-wave plans' stages (32 KiB tiles at d = 128, three stages in the
+    // ping-pong schedule) reach past 64 KiB, where a read's position no longer fits the 16-bit
+    // offset field of ds_read and every read would add it to its address register; there the
+    // K and V tiles are arrays of their own, K first, so the K reads of every stage lie in the
+    // first 64 KiB, and the V reads take their tiles' position in their base registers.
+    struct Stage {
+        lds_u8* k;
+        lds_u8* v;
+    };
+    constexpr bool kSplitKV = WAVES == 8;
+    Stage stage0, stage1, stage2{nullptr, nullptr};   // (stage2: the ping-pong schedule's third)
+    if constexpr (kSplitKV) {
+        __shared__ __attribute__((aligned(1024))) unsigned char k0_raw[TILE];
+        __shared__ __attribute__((aligned(1024))) unsigned char k1_raw[TILE];
+        if constexpr (PP) {
+            __shared__ __attribute__((aligned(1024))) unsigned char k2_raw[TILE];
+            __shared__ __attribute__((aligned(1024))) unsigned char v2_raw[TILE];
+            stage2 = Stage{(lds_u8*)k2_raw, (lds_u8*)v2_raw};
+        }
+        __shared__ __attribute__((aligned(1024))) unsigned char v0_raw[TILE];
+        __shared__ __attribute__((aligned(1024))) unsigned char v1_raw[TILE];
+        stage0 = Stage{(lds_u8*)k0_raw, (lds_u8*)v0_raw};
+        stage1 = Stage{(lds_u8*)k1_raw, (lds_u8*)v1_raw};
+    } else {
+        __shared__ __attribute__((aligned(1024))) unsigned char stage0_raw[2 * TILE];
+        __shared__ __attribute__((aligned(1024))) unsigned char stage1_raw[2 * TILE];
+        stage0 = Stage{(lds_u8*)stage0_raw, (lds_u8*)stage0_raw + TILE};
+        stage1 = Stage{(lds_u8*)stage1_raw, (lds_u8*)stage1_raw + TILE};
     }
+    // the four tile arrays of stages 0 and 1, in turn (staging areas of the epilogue and the
+    // last-block key split)
+    auto area = [&](int i) -> lds_u8* { return i == 0 ? stage0.k : i == 1 ? stage0.v : i == 2 ? stage1.k : stage1.v; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -154,7 +176,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
             for (int db = 0; db < DB; ++db) {
                 const int key = 8 * aa + 4 * h + (r >> 2);
                 const int dim = 32 * db + 16 * (g & 1) + 4 * (r & 3);
-                voff[aa][db] = TILE + key * RB + 16 * ((dim >> 3) ^ swz<CPR>(key)) + 2 * (dim & 7);
+                // (from the V tile; from the stage's K tile where V follows it in one array)
+                voff[aa][db] = (kSplitKV ? 0 : TILE) + key * RB + 16 * ((dim >> 3) ^ swz<CPR>(key)) + 2 * (dim & 7);
             }
     }
 
@@ -181,7 +204,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     constexpr int kTileLoads = 2 * LOADS;
     static_assert(kTileLoads < 64, "vmcnt is six bits");
     constexpr unsigned kWaitOneTileInFlight = 0x0F70u | (kTileLoads & 15) | ((kTileLoads >> 4) << 14);
-    auto issue_tile = [&](int j, lds_u8* stage) {
+    auto issue_tile = [&](int j, const Stage& st) {
         const int soff = j * BC * RB;
 #if defined(FA_LDS_POISON)
         // Debug build: the 16 bytes each copy below will deliver first hold NaN (all-ones
@@ -189,18 +212,18 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         // or barrier -- turns into NaN outputs instead of stale, plausible data.
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            lds_u8* kdst = stage + i * (NT * 16) + wave * 1024 + lane * 16;
-            *reinterpret_cast<lds_u32x4*>(kdst) = u32x4{~0u, ~0u, ~0u, ~0u};
-            *reinterpret_cast<lds_u32x4*>(kdst + TILE) = u32x4{~0u, ~0u, ~0u, ~0u};
+            const int at = i * (NT * 16) + wave * 1024 + lane * 16;
+            *reinterpret_cast<lds_u32x4*>(st.k + at) = u32x4{~0u, ~0u, ~0u, ~0u};
+            *reinterpret_cast<lds_u32x4*>(st.v + at) = u32x4{~0u, ~0u, ~0u, ~0u};
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the poison lands before the copies
 #endif
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            lds_u8* kdst = stage + i * (NT * 16) + wave * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kdst, 16,
+            const int at = i * (NT * 16) + wave * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(st.k + at), 16,
                                                      src_off[i] + soff, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(kdst + TILE), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(st.v + at), 16,
                                                      src_off[i] + soff, 0, 0, 0);
         }
     };
@@ -358,9 +381,32 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     auto pv = [&](const lds_u8* sbase) __attribute__((always_inline)) {
         pv_from(sbase, [&](int aa, int db) { return voff[aa][db]; });
     };
-    auto compute_tile = [&](int j, const lds_u8* sbase) __attribute__((always_inline)) {
-        qk_soft(j, sbase);
-        pv(sbase);
+    // Split layout: the V reads address from stage 0's K tile, with V's position (past the
+    // first 64 KiB) inside the base registers vrel, which an empty asm makes opaque so the
+    // compiler cannot split the constant back out of them; what remains, the stage's and the
+    // k-step's offsets, fits the instruction's offset field.
+    int vrel[2][DB];
+    if constexpr (kSplitKV) {
+        const int vk = (int)(uintptr_t)stage0.v - (int)(uintptr_t)stage0.k;
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                vrel[aa][db] = voff[aa][db] + vk;
+                asm volatile("" : "+v"(vrel[aa][db]));
+            }
+    }
+    auto pv_stage = [&](const Stage& st) __attribute__((always_inline)) {
+        if constexpr (kSplitKV) {
+            const int dv = (int)(uintptr_t)st.v - (int)(uintptr_t)stage0.v;
+            pv_from(stage0.k, [&](int aa, int db) { return vrel[aa][db] + dv; });
+        } else {
+            pv(st.k);
+        }
+    };
+    auto compute_tile = [&](int j, const Stage& st) __attribute__((always_inline)) {
+        qk_soft(j, st.k);
+        pv_stage(st);
     };
 
     // Ping-pong schedule (d = 64, where the softmax takes longer than the MFMAs): every wave
@@ -373,13 +419,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     // groups are done with it by then (the late group's last read, V of tile j - 2, comes
     // before the barrier that ends its step j - 1).  So three stages, the loop unrolled by
     // three to keep every stage a distinct array at compile time.
-    auto pp_step = [&](int j, const lds_u8* cur) __attribute__((always_inline)) {
-        if (has_rows) qk_soft(j, cur);
+    auto pp_step = [&](int j, const Stage& cur) __attribute__((always_inline)) {
+        if (has_rows) qk_soft(j, cur.k);
         if (late) {
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's copies have landed
             __syncthreads();
         }
-        if (has_rows) pv(cur);
+        if (has_rows) pv_stage(cur);
         if (!late) {
             __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
@@ -393,7 +439,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
             // as the LDS reads of the other blocks), so the waves meet only at the merge.
             const int per = (n_tiles + WAVES - 1) / WAVES;
             const int tb = min(n_tiles, wave * per), te = min(n_tiles, tb + per);
-            lds_u8* const region = (wave < 2 ? stage0 : stage1) + (wave & 1) * TILE;
+            lds_u8* const region = area(wave);
             constexpr int VLOADS = TILE / 1024;   // 1 KiB copies per V tile
             auto issue_v = [&](int j) {   // row-major V tile, swizzled as in issue_tile
 #if defined(FA_LDS_POISON)
@@ -442,13 +488,16 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                     issue_v(j + 1);
                 }
             }
-            // Merge into wave 0, one partial at a time: O^T through stage 0 and the row
-            // statistics through tail_stats, both in the accumulator layout, so each lane of
+            // Merge into wave 0, one partial at a time: O^T through stage 0's two tiles and the
+            // row statistics through tail_stats, both in the accumulator layout, so each lane of
             // wave 0 combines the entries of the same lane of wave w.
             __shared__ float tail_stats[3 * 64];
             typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-            lds_f32x4* const opart = (lds_f32x4*)stage0;
-            static_assert(DB * 4 * 64 * 16 <= STAGE, "a wave's O^T fits in one stage");
+            static_assert(DB * 4 * 64 * 16 <= 2 * TILE, "a wave's O^T fits in stage 0");
+            auto opart = [&](int db, int g) {   // 16-byte slot (db, g) of this lane
+                const int at = ((db * 4 + g) * 64 + lane) * 16;
+                return (lds_f32x4*)(at < TILE ? stage0.k + at : stage0.v + (at - TILE));
+            };
 #pragma unroll 1
             for (int w = 1; w < WAVES; ++w) {
                 __syncthreads();
@@ -457,8 +506,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                     for (int db = 0; db < DB; ++db)
 #pragma unroll
                         for (int g = 0; g < 4; ++g)
-                            opart[(db * 4 + g) * 64 + lane] =
-                                f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+                            *opart(db, g) = f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
                     tail_stats[lane] = m;
                     tail_stats[64 + lane] = lsum;
                     tail_stats[128 + lane] = lrnd;
@@ -475,7 +523,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                     for (int db = 0; db < DB; ++db)
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            const f32x4 x = opart[(db * 4 + g) * 64 + lane];
+                            const f32x4 x = *opart(db, g);
 #pragma unroll
                             for (int e = 0; e < 4; ++e) o[db][4 * g + e] = o[db][4 * g + e] * a0 + x[e] * aw;
                         }
@@ -563,8 +611,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     // ping-pong schedule the late group's last P V reads a stage after its last tile barrier).
     __syncthreads();
     if (has_rows && (!tail_split || wave == 0)) {
-        constexpr int WPS = BC / 16;               // waves whose 32 rows fit in one stage
-        lds_u8* obuf = (wave / WPS == 0 ? stage0 : stage1) + (wave % WPS) * (QPW * RB);
+        constexpr int WPT = BC / 32;               // waves whose 32 rows fit in one tile
+        static_assert(WAVES <= 4 * WPT, "the four tiles of stages 0 and 1 stage every wave's rows");
+        lds_u8* obuf;
+        if constexpr (kSplitKV) obuf = area(wave / WPT) + (wave % WPT) * (QPW * RB);
+        else obuf = (wave / (2 * WPT) == 0 ? stage0.k : stage1.k) + (wave % (2 * WPT)) * (QPW * RB);
         // Staging layout: 16-byte chunk c of row r sits in slot c ^ ochunk(r) and its two
         // 8-byte halves are swapped when ohalf(r) is set.  A write instruction puts one
         // 8-byte piece of each of the wave's 32 rows; with this layout the pieces of any 16
