@@ -294,18 +294,33 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
     int n_tiles = (N + BC - 1) / BC;
     if (CAUSAL) n_tiles = min(n_tiles, (min(N, (qblk + 1) * BR) + BC - 1) / BC);
 
+    // Per 64-key block: the K scale folded into c, the V scale as an exponent shift of P and
+    // the inverse factor for the sums.  They are the same for every lane, but there is no
+    // scalar float arithmetic, so derived per tile they cost about ten VALU instructions in a
+    // kernel bound by its VALU work.  Instead lane L derives block 64 c + L's, for 64 blocks
+    // at a time (chunk c), and each tile reads its block's back with v_readlane.
+    float ck_l = 0.f, vshe_l = 0.f, vw_l = 0.f;
+    int chunk = -1;
+    auto lane_value = [](float x, int l) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+    };
     auto compute_tile = [&](int j, const lds_u8* sbase) {
         const int kbase = j * BC;
-        // per 64-key block of this tile: the K scale folded into c, the V scale as an
-        // exponent shift of P and the inverse factor for the sums
         float ck[KS], vsh_e[KS], vw[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int blk = min(j * KS + s, NB - 1);
-            ck[s] = fmaxf(cw * ksh[blk], 1.17549435e-38f);
-            const int sh = max(__builtin_amdgcn_frexp_expf(vsh[blk]) - 1 - ev_max, kFp8MinVShift);
-            vsh_e[s] = (float)sh + kFp8POffset;
-            vw[s] = __builtin_amdgcn_ldexpf(1.0f, -sh);
+            if (blk >> 6 != chunk) {   // uniform: once per 64 blocks
+                chunk = blk >> 6;
+                const int lb = min(64 * chunk + lane, NB - 1);
+                ck_l = fmaxf(cw * ksh[lb], 1.17549435e-38f);
+                const int sh = max(__builtin_amdgcn_frexp_expf(vsh[lb]) - 1 - ev_max, kFp8MinVShift);
+                vshe_l = (float)sh + kFp8POffset;
+                vw_l = __builtin_amdgcn_ldexpf(1.0f, -sh);
+            }
+            ck[s] = lane_value(ck_l, blk & 63);
+            vsh_e[s] = lane_value(vshe_l, blk & 63);
+            vw[s] = lane_value(vw_l, blk & 63);
         }
 
         __builtin_amdgcn_s_setprio(1);
@@ -352,14 +367,19 @@ __global__ __launch_bounds__(64 * WAVES, 3) void fwd_fp8_kernel(Fp8Args a) {
             float tsum;
             auto make_p = [&](float neg_m) {
                 const float nm = neg_m + vsh_e[ks];
-                float acc0 = 0.f, acc1 = 0.f;
+                float acc0, acc1;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     float p[16];
 #pragma unroll
                     for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(s[2 * ks + kk][t], ck[ks], nm));
+                    // (the sums start from their first terms: 0 + p is an instruction the
+                    // compiler may not drop, as it would turn -0 into +0)
 #pragma unroll
-                    for (int t = 0; t < 16; t += 2) { acc0 += p[t]; acc1 += p[t + 1]; }
+                    for (int t = 0; t < 16; t += 2) {
+                        acc0 = kk == 0 && t == 0 ? p[t] : acc0 + p[t];
+                        acc1 = kk == 0 && t == 0 ? p[t + 1] : acc1 + p[t + 1];
+                    }
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         pb[2 * q + kk] = (int)pack4_fp8(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3], pb[2 * q + kk]);
