@@ -303,8 +303,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
 #pragma unroll
                 for (int t = 0; t < 16; ++t) p[t] = fast_exp2(__builtin_fmaf(s[kb][t], c, neg_m));
                 if constexpr (!ONE_SUM) {
+                    // (from the first terms: 0 + p is an add the compiler may not drop)
 #pragma unroll
-                    for (int t = 0; t < 16; t += 2) { acc0 += p[t]; acc1 += p[t + 1]; }
+                    for (int t = 0; t < 16; t += 2) {
+                        acc0 = kb == 0 && t == 0 ? p[t] : acc0 + p[t];
+                        acc1 = kb == 0 && t == 0 ? p[t + 1] : acc1 + p[t + 1];
+                    }
                 }
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
