@@ -315,14 +315,29 @@ def wl_dtype_code(dtype):
 
 # ------------------------------------------------------------ non-finite inputs ---
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-def test_non_finite_inputs_propagate(gpu_lib, dtype):
+NON_FINITE_CASES = [
+    # (dtype, N, d, FA_TILE, query rows poisoned, key row poisoned, value row poisoned)
+    ("bf16", 300, 64, "", 77, 140, 200, 31),
+    ("fp16", 300, 64, "", 77, 140, 200, 31),
+    ("fp32", 300, 64, "", 77, 140, 200, 31),
+    # one-row last block whose waves split the keys (37 tiles): the NaN key lies in the last
+    # wave's quarter, so it must survive the merge into wave 0; the Inf row is that block's
+    ("bf16", 1153, 128, "128,32,4", 77, 1152, 1000, 31),
+    ("fp16", 1153, 128, "128,32,4", 77, 1152, 1000, 31),
+]
+
+
+@pytest.mark.parametrize("dtype,N,d,tile,qnan,qinf,knan,vnan", NON_FINITE_CASES,
+                         ids=[f"{c[0]}-N{c[1]}-d{c[2]}" for c in NON_FINITE_CASES])
+def test_non_finite_inputs_propagate(gpu_lib, monkeypatch, dtype, N, d, tile, qnan, qinf, knan, vnan):
     """A NaN or Inf in query row i reaches row i's output and LSE only; a NaN in key row j
     reaches every row (each score row contains key j); a NaN in value row j reaches every
     output row but no LSE.  Rows not touched stay equal to the oracle."""
     import torch
 
-    N, d = 300, 64
+    if tile:
+        monkeypatch.setenv("FA_TILE", tile)
+        assert gpu_lib.fa_fwd_plan(1, 1, N, d, wl_dtype_code(dtype))["tail_kv_splits"] == 4
     q, k, v = _random_qkv(1, 1, N, d, dtype, seed=7)
     O_ref, L_ref = _oracle_full(q, k, v, scale_of(d))
     cases = {
@@ -331,16 +346,16 @@ def test_non_finite_inputs_propagate(gpu_lib, dtype):
         "k row NaN": (q, k.copy(), v, "k"),
         "v row NaN": (q, k, v.copy(), "v"),
     }
-    cases["q row NaN"][0][0, 0, 77, 5] = np.nan
-    cases["q row Inf"][0][0, 0, 140, 3] = np.inf
-    cases["k row NaN"][1][0, 0, 200, 9] = np.nan
-    cases["v row NaN"][2][0, 0, 31, 2] = np.nan
+    cases["q row NaN"][0][0, 0, qnan, 5] = np.nan
+    cases["q row Inf"][0][0, 0, qinf, 3] = np.inf
+    cases["k row NaN"][1][0, 0, knan, 9] = np.nan
+    cases["v row NaN"][2][0, 0, vnan, 2] = np.nan
     for name, (qq, kk, vv, kind) in cases.items():
         O, L = run_fwd(gpu_lib, qq, kk, vv, dtype)
         bad_o = ~np.isfinite(O[0, 0])
         bad_l = ~np.isfinite(L[0, 0])
         if kind in ("q", "qinf"):
-            row = 77 if kind == "q" else 140
+            row = qnan if kind == "q" else qinf
             assert bad_o[row].all() or bad_l[row], f"{name}: row {row} stayed finite"
             others = np.arange(N) != row
             assert not bad_o[others].any() and not bad_l[others].any(), f"{name}: leaked to other rows"
