@@ -29,7 +29,9 @@
 //    taken.  Exact softmax does not depend on m (the same m is used for l, O and LSE),
 //    which only has to keep P finite and in range: a tile is redone with its own maximum,
 //    and O and l rescaled, only when a row's sum of P over the tile leaves [0, 2^15] --
-//    the first tile (m = -inf) or a maximum that jumped.
+//    the first tile (m = -inf) or a maximum that jumped.  In bf16 the redone tile sets m 8
+//    above its maximum (P <= 2^-8 there; bf16 keeps fp32's exponent range), so the next
+//    redo needs a jump of more than 23.
 //  * LDS tiles use an XOR swizzle of 16-byte chunks so the 16 lanes that read one
 //    chunk column of consecutive rows hit distinct banks.
 //  * Workgroup ids are remapped so consecutive query blocks of one head land on the
@@ -290,10 +292,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         }
 
         // ---- P = 2^(s*c - m), packed; the O divisor sums the rounded values, LSE the fp32
-        // ones (fp16: the rounded sum serves both).  P is first formed with the running maximum m as it stands: the exact softmax
-        // does not depend on m, which only has to keep P finite and in range.  A tile is
-        // redone with its own maximum when some row's tile sum leaves [0, 2^15] -- the first
-        // tile (m = -inf), or a row maximum that jumped by more than 15 in base-2 units.
+        // ones (fp16: the rounded sum serves both).  P is first formed with the running
+        // maximum m as it stands: the exact softmax does not depend on m, which only has to
+        // keep P finite and in range.  A tile is redone with its own maximum (plus the bf16
+        // headroom) when some row's tile sum leaves [0, 2^15] -- the first tile (m = -inf),
+        // or a row maximum that jumped by more than 15 (bf16: 23) in base-2 units.
         float acc0, acc1, racc0, racc1;
         auto make_p = [&](float neg_m) {
             acc0 = 0.f, acc1 = 0.f, racc0 = 0.f, racc1 = 0.f;
@@ -339,7 +342,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                     x0 = vmax3(x0, s[kb][t], s[kb][t + 1]);
                     x1 = vmax3(x1, s[kb][t + 2], s[kb][t + 3]);
                 }
-            const float mx = pair_max(__builtin_elementwise_maximum(x0, x1)) * c;
+            const float xm = pair_max(__builtin_elementwise_maximum(x0, x1));
+            const float mx = ONE_SUM ? xm * c : __builtin_fmaf(xm, c, a.m_headroom);
             const float mnew = fmaxf(m, mx);
             const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
             m = mnew;

@@ -24,6 +24,12 @@ struct FwdArgs {
     int n_qblk;     // ceil(n / Br)
     int n_blocks;   // workgroups in the grid = B*H*n_qblk (*splits)
     float c;        // scale * log2(e): scores are taken to base 2 inside the kernel
+    // bf16/fp16 forward: a redone tile sets the running maximum this far (base 2) above its own
+    // maximum, so P stays at most 2^-8 there and later tiles need a larger jump to be redone.
+    // (An argument, so it sits in a scalar register: as a literal the compiler holds it in a
+    // vector register, and the 168-register kernels then spill.)  fp16 uses none: its P
+    // would lose range to underflow.
+    float m_headroom = 8.f;
     // split-KV only: key tiles [s*tiles_per_split, (s+1)*tiles_per_split) per split s;
     // normalised fp32 partial O [splits][B*H*N][d] and partial LSE [splits][B*H*N]
     int splits;
