@@ -672,29 +672,55 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
 // Combines the normalised partials of the key ranges by their log-sum-exp, the two-block
 // merge of "FlashAttention 硬件感知计算剖析" (section 二) generalised to S parts:
 //     LSE = ln sum_s e^{LSE_s},   O = sum_s e^{LSE_s - LSE} O_s.
-// D / 8 lanes per row, 8 dims (two 16-byte loads per partial) each.
+// D / 8 lanes per row, 8 dims (two 16-byte loads per partial) each.  The parts are taken eight
+// at a time, their loads issued together, and folded in with a running maximum (the same
+// merge applied chunk by chunk), so a row costs one pass over its partials.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ o_part,
                                                             const float* __restrict__ lse_part, T* __restrict__ O,
                                                             float* __restrict__ LSE, int64_t rows, int splits) {
-    constexpr int LPR = D / 8, RPB = 256 / LPR;
+    constexpr int LPR = D / 8, RPB = 256 / LPR, CH = 8;
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
     if (row >= rows) return;
-    float mx = -INFINITY;
-    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, lse_part[(int64_t)s * rows + row]);
-    float den = 0.f;
-    for (int s = 0; s < splits; ++s) den += __expf(lse_part[(int64_t)s * rows + row] - mx);
-    const float lse = mx + __logf(den);
+    float mx = -INFINITY, den = 0.f;
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s) {
-        const float w = __expf(lse_part[(int64_t)s * rows + row] - lse);
-        const float* src = o_part + ((int64_t)s * rows + row) * D + part * 8;
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-        a0 += w * x0;
-        a1 += w * x1;
+    for (int s0 = 0; s0 < splits; s0 += CH) {
+        float l[CH];
+        f32x4 x0[CH], x1[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            l[i] = -INFINITY;
+            x0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            x1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (s0 + i < splits) {
+                const int64_t pr = (int64_t)(s0 + i) * rows + row;
+                l[i] = lse_part[pr];
+                x0[i] = *reinterpret_cast<const f32x4*>(o_part + pr * D + part * 8);
+                x1[i] = *reinterpret_cast<const f32x4*>(o_part + pr * D + part * 8 + 4);
+            }
+        }
+        float cm = mx;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) cm = fmaxf(cm, l[i]);
+        if (cm == -INFINITY) continue;   // only empty key ranges so far (LSE_s = -inf, O_s = 0)
+        const float r = __expf(mx - cm);   // 0 while mx = -inf
+        den *= r;
+        a0 *= r;
+        a1 *= r;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const float w = __expf(l[i] - cm);
+            den += w;
+            a0 += w * x0[i];
+            a1 += w * x1[i];
+        }
+        mx = cm;
     }
+    const float lse = mx + __logf(den);
+    const float inv = 1.f / den;
+    a0 *= inv;
+    a1 *= inv;
     u32x4 out;
     out[0] = Elt<T>::pack2(a0[0], a0[1]);
     out[1] = Elt<T>::pack2(a0[2], a0[3]);
