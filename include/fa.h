@@ -106,12 +106,20 @@ typedef struct {
     int32_t waves;          /* wavefronts (64 lanes) per workgroup                     */
     int32_t rows_per_wave;  /* query rows each wave computes                           */
     int32_t lds_bytes;      /* LDS per workgroup (its K and V tile buffers)            */
-    int64_t grid;           /* workgroups launched = B*H*ceil(N/Br) (*splits)          */
+    int64_t grid;           /* workgroups launched = B*H*ceil(N/Br) (*splits); with    */
+                            /* tail first (below) B*H*floor(N/Br)                      */
     int32_t kv_splits;      /* >1: key range split across workgroups, then merged      */
     int32_t wave_kv_splits; /* >1: a workgroup's waves share its query rows and split  */
                             /*     the key tiles among themselves, merged in LDS       */
-    int32_t tail_kv_splits; /* >1: the same for the last query block of each head only */
-                            /*     (at most 32 rows; whole grid resident at once)      */
+    int32_t tail_kv_splits; /* >1: the last query block of each head (at most 32 rows) */
+                            /*     has its keys split.  4 waves: over the block's      */
+                            /*     waves, merged in LDS (whole grid resident at once). */
+                            /*     8 waves ("tail first"): those rows are computed     */
+                            /*     ahead of the main launch by tail_kv_splits          */
+                            /*     workgroups per head, their partials parked in the   */
+                            /*     head's first O rows and merged; the main launch     */
+                            /*     then covers the full blocks (not used when O        */
+                            /*     overlaps Q, K, V or LSE)                            */
 } fa_plan;
 
 /*

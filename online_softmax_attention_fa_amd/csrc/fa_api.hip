@@ -86,11 +86,17 @@ fa_status make_plan(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int c
     const char* tile = getenv("FA_TILE");
     *overridden = tile && *tile;
     if (!fa::apply_tile_override(plan, tile, B, H, N, d, dtype, causal)) return FA_ERR_TILE;
-    plan->tail_kv_splits = fa::fwd_tail_kv_splits(*plan, dtype, N, N, d, causal);
+    fa::finalize_tail(plan, dtype, B, H, N, N, d, causal);
     return FA_OK;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Whether the byte ranges [p, p + np) and [q, q + nq) share a byte.
+bool overlaps(const void* p, size_t np, const void* q, size_t nq) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + nq && b < a + np;
+}
 
 // Shape / dtype checks shared by the plan query and the launches.
 fa_status check_problem(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
@@ -123,14 +129,32 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
     st = make_plan(B, H, N, d, dtype, causal, &plan, &overridden);
     if (st != FA_OK) return st;
     if (plan.grid >= kMaxGrid) return FA_ERR_SHAPE;
-    plan.tail_kv_splits = fa::fwd_tail_kv_splits(plan, dtype, N, Nk, d, causal);
-    if (log_enabled())
+    fa::finalize_tail(&plan, dtype, B, H, N, Nk, d, causal);
+    // Tail first parks its partials in O ahead of the main launch: not when O shares memory
+    // with an input (or the LSE), which would then be overwritten before it is read.
+    const size_t elt = dtype == FA_F32 ? 4 : 2, qo_bytes = (size_t)(B * H * N * d) * elt;
+    const size_t kv_bytes = (size_t)(B * H * Nk * d) * elt, lse_bytes = (size_t)(B * H * N) * sizeof(float);
+    bool tail_first = plan.waves == 8 && plan.tail_kv_splits > 1;
+    if (tail_first && (overlaps(O, qo_bytes, Q, qo_bytes) || overlaps(O, qo_bytes, K, kv_bytes) ||
+                       overlaps(O, qo_bytes, V, kv_bytes) || overlaps(O, qo_bytes, LSE, lse_bytes))) {
+        tail_first = false;
+        plan.tail_kv_splits = 1;
+        plan.grid = B * H * fa::ceil_div(N, plan.block_q);
+    }
+    const int64_t n_main = tail_first ? N / 256 * 256 : N;
+    if (log_enabled()) {
+        char tail_note[96] = "";
+        if (tail_first)
+            snprintf(tail_note, sizeof tail_note, " (the last %lld rows first: %d key ranges per head, merged)",
+                     (long long)(N - n_main), plan.tail_kv_splits);
+        else if (plan.tail_kv_splits > 1)
+            snprintf(tail_note, sizeof tail_note, " (the last block's waves split the key tiles)");
         fprintf(stderr, "fa_fwd%s: B=%lld H=%lld N=%lld Nk=%lld d=%lld %s -> Br=%d Bc=%d waves=%d grid=%lld lds=%d%s%s%s\n",
                 causal ? "_causal" : "", (long long)B, (long long)H, (long long)N, (long long)Nk, (long long)d,
                 dtype_name(dtype), plan.block_q, plan.block_k, plan.waves, (long long)plan.grid, plan.lds_bytes,
-                plan.wave_kv_splits > 1 ? " (waves split the key tiles)" : "",
-                plan.tail_kv_splits > 1 ? " (the last block's waves split the key tiles)" : "",
+                plan.wave_kv_splits > 1 ? " (waves split the key tiles)" : "", tail_note,
                 overridden ? " (FA_TILE)" : "");
+    }
     st = check_device();
     if (st != FA_OK) return st;
 
@@ -142,13 +166,46 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
     a.lse = LSE;
     a.n = (int)N;
     a.nk = (int)Nk;
-    a.n_qblk = (int)fa::ceil_div(N, plan.block_q);
+    a.n_qblk = (int)(tail_first ? n_main / plan.block_q : fa::ceil_div(N, plan.block_q));
     a.n_blocks = (int)plan.grid;
     a.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
     a.splits = 1;
     a.tiles_per_split = 0;
     a.o_part = nullptr;
     a.lse_part = nullptr;
+    if (tail_first) {
+        // the last r rows of every head: split-KV partials parked in the head's first O rows,
+        // merged into its rows n_main .. N - 1, ahead of the main launch that overwrites them
+        const int S = plan.tail_kv_splits;
+        const int64_t r = N - n_main, tiles = fa::ceil_div(N, fa::splitkv_block_k(d));
+        fa::FwdArgs t = a;
+        t.qblk0 = (int)(n_main / 128);
+        t.n_qblk = 1;
+        t.splits = S;
+        t.tiles_per_split = (int)fa::ceil_div(tiles, S);
+        t.n_blocks = (int)(B * H * S);
+        t.o_part = reinterpret_cast<float*>(O);
+        t.lse_part = t.o_part + (int64_t)S * r * d;
+        t.po_head = t.pl_head = N * d * (int64_t)elt / (int64_t)sizeof(float);
+        t.po_split = r * d;
+        t.pl_split = r;
+        t.part_row0 = (int)n_main;
+        fa::MergeArgs m;
+        m.o_part = t.o_part;
+        m.lse_part = t.lse_part;
+        m.o = O;
+        m.lse = LSE;
+        m.rows = B * H * r;
+        m.rows_per_head = (int)r;
+        m.splits = S;
+        m.po_head = t.po_head;
+        m.po_split = t.po_split;
+        m.pl_head = t.pl_head;
+        m.pl_split = t.pl_split;
+        m.out_head = N;
+        m.out_row0 = (int)n_main;
+        if (fa_launch_fwd_splitkv(t, m, dtype, (int)d, stream) != 0) return FA_ERR_LAUNCH;
+    }
     const int e = fa_launch_fwd(a, plan, dtype, (int)d, causal, stream);
     return e == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -225,7 +282,25 @@ fa_status splitkv_common(const void* Q, const void* K, const void* V, void* O, f
     const size_t o_bytes = (size_t)splits * (size_t)(B * H * N) * (size_t)d * sizeof(float);
     a.o_part = reinterpret_cast<float*>(ws);
     a.lse_part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) + (o_bytes + 255) / 256 * 256);
-    const int e = fa_launch_fwd_splitkv(a, B * H * N, dtype, (int)d, stream);
+    a.po_head = N * d;   // [splits][B*H*N][d] and [splits][B*H*N]
+    a.po_split = B * H * N * d;
+    a.pl_head = N;
+    a.pl_split = B * H * N;
+    fa::MergeArgs m;
+    m.o_part = a.o_part;
+    m.lse_part = a.lse_part;
+    m.o = O;
+    m.lse = LSE;
+    m.rows = B * H * N;
+    m.rows_per_head = (int)N;
+    m.splits = splits;
+    m.po_head = a.po_head;
+    m.po_split = a.po_split;
+    m.pl_head = a.pl_head;
+    m.pl_split = a.pl_split;
+    m.out_head = N;
+    m.out_row0 = 0;
+    const int e = fa_launch_fwd_splitkv(a, m, dtype, (int)d, stream);
     return e == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 

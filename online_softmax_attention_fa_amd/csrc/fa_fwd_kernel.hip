@@ -134,6 +134,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     int qblk = rem / nsplit;
     const int split = rem - qblk * nsplit;
     if (CAUSAL) qblk = a.n_qblk - 1 - qblk;   // longest rows first
+    if (SPLIT) qblk += a.qblk0;
     const int64_t head = (int64_t)bh * N * D, khead = (int64_t)bh * NK * D;
     const T* __restrict__ Qh = reinterpret_cast<const T*>(a.q) + head;
     const T* __restrict__ Kh = reinterpret_cast<const T*>(a.k) + khead;
@@ -597,8 +598,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     if (SPLIT) {   // normalised fp32 partials of this key range (an empty range: O 0, LSE -inf)
         if (query < N) {
             const bool empty = t0 >= n_tiles;
-            const int64_t prow = ((int64_t)split * (a.n_blocks / (a.n_qblk * nsplit)) + bh) * N + query;
-            float* orow = a.o_part + prow * D;
+            const int64_t i = query - a.part_row0;
+            float* orow = a.o_part + bh * a.po_head + split * a.po_split + i * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -608,7 +609,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                     for (int e = 0; e < 4; ++e) w[e] = empty ? 0.f : o[db][4 * g + e] * inv;
                     *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * h) = w;
                 }
-            if (h == 0) a.lse_part[prow] = empty ? -INFINITY : (m + __builtin_amdgcn_logf(lt)) * kLn2;
+            if (h == 0)
+                a.lse_part[bh * a.pl_head + split * a.pl_split + i] =
+                    empty ? -INFINITY : (m + __builtin_amdgcn_logf(lt)) * kLn2;
         }
         return;
     }
@@ -676,13 +679,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
 // at a time, their loads issued together, and folded in with a running maximum (the same
 // merge applied chunk by chunk), so a row costs one pass over its partials.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ o_part,
-                                                            const float* __restrict__ lse_part, T* __restrict__ O,
-                                                            float* __restrict__ LSE, int64_t rows, int splits) {
+__global__ __launch_bounds__(256) void splitkv_merge_kernel(MergeArgs a) {
     constexpr int LPR = D / 8, RPB = 256 / LPR, CH = 8;
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
-    if (row >= rows) return;
+    if (row >= a.rows) return;
+    const int64_t bh = row / a.rows_per_head, i = row - bh * a.rows_per_head;
+    const float* __restrict__ o_part = a.o_part + bh * a.po_head + i * D;
+    const float* __restrict__ lse_part = a.lse_part + bh * a.pl_head + i;
+    const int splits = a.splits;
     float mx = -INFINITY, den = 0.f;
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < splits; s0 += CH) {
@@ -694,10 +699,10 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restr
             x0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             x1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (s0 + i < splits) {
-                const int64_t pr = (int64_t)(s0 + i) * rows + row;
-                l[i] = lse_part[pr];
-                x0[i] = *reinterpret_cast<const f32x4*>(o_part + pr * D + part * 8);
-                x1[i] = *reinterpret_cast<const f32x4*>(o_part + pr * D + part * 8 + 4);
+                const int64_t s = s0 + i;
+                l[i] = lse_part[s * a.pl_split];
+                x0[i] = *reinterpret_cast<const f32x4*>(o_part + s * a.po_split + part * 8);
+                x1[i] = *reinterpret_cast<const f32x4*>(o_part + s * a.po_split + part * 8 + 4);
             }
         }
         float cm = mx;
@@ -726,18 +731,18 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restr
     out[1] = Elt<T>::pack2(a0[2], a0[3]);
     out[2] = Elt<T>::pack2(a1[0], a1[1]);
     out[3] = Elt<T>::pack2(a1[2], a1[3]);
-    *reinterpret_cast<u32x4*>(O + row * D + part * 8) = out;
-    if (part == 0) LSE[row] = lse;
+    const int64_t orow = bh * a.out_head + a.out_row0 + i;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<T*>(a.o) + orow * D + part * 8) = out;
+    if (part == 0) a.lse[orow] = lse;
 }
 
 template <typename T, int D, int BC>
-static hipError_t launch_splitkv_t(const FwdArgs& a, int64_t rows, hipStream_t st) {
+static hipError_t launch_splitkv_t(const FwdArgs& a, const MergeArgs& m, hipStream_t st) {
     hipLaunchKernelGGL((fwd_kernel<T, D, BC, 4, false, true>), dim3((unsigned)a.n_blocks), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((splitkv_merge_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                       a.o_part, a.lse_part, reinterpret_cast<T*>(a.o), a.lse, rows, a.splits);
+    hipLaunchKernelGGL((splitkv_merge_kernel<T, D>), dim3((unsigned)((m.rows + RPB - 1) / RPB)), dim3(256), 0, st, m);
     return hipGetLastError();
 }
 
@@ -926,7 +931,7 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
 
 // ------------------------------------------------------------------ dispatch ---
 
-// tail: the plan's last-block key split (non-causal 4-wave plans only)
+// tail: the plan's last-block key split on a 4-wave plan (its waves share the block's rows)
 template <typename T, int D, int BC, int WAVES>
 static hipError_t launch_t(const FwdArgs& a, int causal, bool tail, hipStream_t st) {
     const dim3 grid((unsigned)a.n_blocks), block(64 * WAVES);
@@ -946,7 +951,9 @@ static hipError_t launch_t(const FwdArgs& a, int causal, bool tail, hipStream_t 
 // The compiled (d, Bc, waves) shapes; the chooser only emits these.
 template <typename T>
 static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int causal, hipStream_t st) {
-    const bool tail = p.tail_kv_splits > 1;
+    // (an 8-wave plan's tail_kv_splits is the tail-first split count: its last rows were
+    // computed by the split-KV launches ahead of this one)
+    const bool tail = p.waves == 4 && p.tail_kv_splits > 1;
     if (d == 128 && p.block_k == 128 && p.waves == 8) return launch_t<T, 128, 128, 8>(a, causal, tail, st);
     if (d == 64 && p.block_k == 128 && p.waves == 8) {
         if (causal) return launch_t<T, 64, 128, 8>(a, causal, false, st);
@@ -963,13 +970,13 @@ static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int cau
 
 }  // namespace fa
 
-int fa_launch_fwd_splitkv(const fa::FwdArgs& a, int64_t rows, int dtype, int d, hipStream_t st) {
+int fa_launch_fwd_splitkv(const fa::FwdArgs& a, const fa::MergeArgs& m, int dtype, int d, hipStream_t st) {
     using namespace fa;
     hipError_t e;
     if (dtype == FA_BF16)
-        e = d == 128 ? launch_splitkv_t<__bf16, 128, 64>(a, rows, st) : launch_splitkv_t<__bf16, 64, 128>(a, rows, st);
+        e = d == 128 ? launch_splitkv_t<__bf16, 128, 64>(a, m, st) : launch_splitkv_t<__bf16, 64, 128>(a, m, st);
     else
-        e = d == 128 ? launch_splitkv_t<_Float16, 128, 64>(a, rows, st) : launch_splitkv_t<_Float16, 64, 128>(a, rows, st);
+        e = d == 128 ? launch_splitkv_t<_Float16, 128, 64>(a, m, st) : launch_splitkv_t<_Float16, 64, 128>(a, m, st);
     return (int)e;
 }
 

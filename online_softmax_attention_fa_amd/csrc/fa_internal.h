@@ -31,11 +31,34 @@ struct FwdArgs {
     // would lose range to underflow.
     float m_headroom = 8.f;
     // split-KV only: key tiles [s*tiles_per_split, (s+1)*tiles_per_split) per split s;
-    // normalised fp32 partial O [splits][B*H*N][d] and partial LSE [splits][B*H*N]
+    // normalised fp32 partials, that of head bh, split s and query row part_row0 + i at
+    // o_part + bh*po_head + s*po_split + i*d (d floats) and lse_part + bh*pl_head + s*pl_split + i
+    // (a split-KV call: [splits][B*H*N][d] and [splits][B*H*N]; the tail rows ahead of an
+    // 8-wave launch: per head, in the first rows of that head's O).  The grid covers query
+    // blocks qblk0 .. qblk0 + n_qblk - 1 of each head.
     int splits;
     int tiles_per_split;
     float* o_part;
     float* lse_part;
+    int64_t po_head = 0, po_split = 0, pl_head = 0, pl_split = 0;
+    int part_row0 = 0;
+    int qblk0 = 0;
+};
+
+// Arguments of the split-KV merge: `rows` merged rows, rows_per_head of them per head (head
+// bh's row i is output row out_row0 + i of that head, whose O and LSE hold out_head rows);
+// partials laid out as in FwdArgs.
+struct MergeArgs {
+    const float* o_part;
+    const float* lse_part;
+    void* o;
+    float* lse;
+    int64_t rows;
+    int rows_per_head;
+    int splits;
+    int64_t po_head, po_split, pl_head, pl_split;
+    int64_t out_head;
+    int out_row0;
 };
 
 // Kernel arguments of the backward pass.
@@ -118,6 +141,52 @@ inline double grid_time(int64_t w, double unit, int per_cu, const double* eff) {
     return t;
 }
 
+// Key tile of the split-KV path (the 4-wave tile-loop kernel's Bc).
+inline int splitkv_block_k(int64_t d) { return d == 128 ? 64 : 128; }
+
+// Last rows ahead of an 8-wave launch ("tail first").  When N = 256 k + r with 1 <= r <= 32,
+// the 8-wave grid's last block of each head holds r rows on its first wave, which sweeps every
+// key alone: on a grid of whole rounds those blocks make a round of their own.  Instead the r
+// rows of every head are computed first by the split-KV kernel, S workgroups per head over
+// S key ranges, their normalised partials parked in the first rows of that head's O (which
+// the 8-wave launch overwrites later, in stream order), and merged into O and the LSE by the
+// merge kernel; the 8-wave launch then covers the k full blocks only.  S aims at 256
+// workgroups in all and at most 16 key tiles per range, within what the parked partials may
+// occupy: 4 S r (d + 1) bytes of the head's 256 k d 2 bytes of O.  Measured against the
+// plans before it (interleaved, N(0,1) inputs unless noted): B2 H8 N4097 d128 151.4 -> 139.2
+// us (edge workload heads 161.4 -> 150.8), B4 H8 N4097 292.5 -> 265.5, B2 H4 N8193 275.3 ->
+// 256.1, B2 H16 N4097 d64 182.5 -> 162.8, B2 H8 N16385 2.05 -> 1.88 ms, B8 H8 N4097 527 ->
+// 505 us.  The tail rows read every head's K and V once more, so with many heads the
+// launches cost more than the round they save (B16 H64 N2049: 2.13 ms on the 4-wave plan,
+// 2.33 ms this way); tail_first_cost prices that.
+constexpr int kTailFirstMaxRows = 32;
+inline int tail_first_splits(int64_t B, int64_t H, int64_t N, int64_t d) {
+    const int64_t full = N / 256, r = N % 256;
+    if (full <= 0 || r < 1 || r > kTailFirstMaxRows || B * H <= 0) return 1;
+    const int64_t tiles = ceil_div(N, splitkv_block_k(d));
+    int64_t s = ceil_div(256, B * H);
+    if (s < ceil_div(tiles, 16)) s = ceil_div(tiles, 16);
+    if (s > 64) s = 64;   // kMaxKvSplits
+    if (s > tiles) s = tiles;
+    const int64_t room = full * 256 * d * 2 / (4 * r * (d + 1));   // partials that fit in O
+    if (s > room) s = room;
+    return s < 2 ? 1 : (int)s;
+}
+// The tail-first launches in units of grid_time (one 256-row block against all N keys): a
+// fixed 8 us, the second pass over every head's K and V at 6 TB/s, and the split workgroups'
+// rounds (two per CU, one busy wave each) at 1 us per key tile; one unit at 4.5 TFLOP/s per
+// CU for d = 128 and 3.6 for d = 64 (the 8-wave kernels' measured rates).  Fitted to the
+// tail launches' share of measured times: about 15 us at B2 H8 N4097, 33 us at B8 H16
+// N2049, 300 us at B16 H64 N2049.
+inline double tail_first_cost(int64_t B, int64_t H, int64_t N, int64_t d, int s) {
+    const double kv_us = (double)(B * H) * (double)N * (double)d * 4.0 / 6e6;
+    const int64_t tiles = ceil_div(N, splitkv_block_k(d));
+    const double rounds = (double)ceil_div(B * H * s, 2 * kCus);
+    const double tail_us = 8.0 + kv_us + rounds * (double)ceil_div(tiles, s) * 1.0;
+    const double unit_us = 256.0 * (double)N * (double)d * 4.0 / (d == 128 ? 4.5e6 : 3.6e6);
+    return tail_us / unit_us;
+}
+
 // The chooser.  Inputs are already validated (d in {64,128}, dtype known, N > 0).
 //
 // bf16/fp16: 32 query rows per wave (one 32-row MFMA column block), two waves per SIMD.
@@ -169,7 +238,11 @@ inline fa_plan choose_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t d, int d
         // Three plans, costed by grid_time: 8 waves (one 256-row workgroup per CU), 4 waves at
         // two workgroups per CU (Bc 64 at d = 128, 128 at d = 64) or at three (Bc 32 / 64).
         const int64_t g8 = B * H * ceil_div(N, 8 * 32), g4 = B * H * ceil_div(N, 4 * 32);
-        const double t8 = grid_time(g8, 1.0, 1, kEff8);
+        double t8 = grid_time(g8, 1.0, 1, kEff8);
+        if (const int s = tail_first_splits(B, H, N, d); s > 1) {   // the last rows ahead of the launch
+            const double first = grid_time(B * H * (N / 256), 1.0, 1, kEff8) + tail_first_cost(B, H, N, d, s);
+            if (first < t8) t8 = first;
+        }
         const double t2 = grid_time(g4, 0.5, 2, kEff4);
         const double t3 = grid_time(g4, 0.5, 3, kEff4);
         if (t8 <= t2 && t8 <= t3) {
@@ -219,8 +292,20 @@ inline int fwd_per_cu(int64_t d, int block_k, int waves) {
 // 8-wave plans (four of the eight waves splitting, the LDS holding four V tiles) it measured
 // within -6% and +2% of the plain kernel: with 128-key tiles each wave's K loads, six in
 // flight from a wave that runs alone, took about 5.6 us per tile.
-inline int fwd_tail_kv_splits(const fa_plan& p, int dtype, int64_t N, int64_t Nk, int64_t d, int causal) {
-    if (dtype == FA_F32 || causal || p.waves != 4 || p.kv_splits > 1 || N <= 0) return 1;
+// On the 8-wave plans the answer is the tail-first split count S (above), when the rows
+// qualify, the problem is self-attention (Nk = N) and the grid it leaves costs less.
+inline int fwd_tail_kv_splits(const fa_plan& p, int dtype, int64_t B, int64_t H, int64_t N, int64_t Nk,
+                              int64_t d, int causal) {
+    if (dtype == FA_F32 || causal || p.kv_splits > 1 || N <= 0) return 1;
+    if (p.waves == 8) {
+        if (Nk != N) return 1;
+        const int s = tail_first_splits(B, H, N, d);
+        if (s <= 1) return 1;
+        const double plain = grid_time(B * H * ceil_div(N, 256), 1.0, 1, kEff8);
+        const double first = grid_time(B * H * (N / 256), 1.0, 1, kEff8) + tail_first_cost(B, H, N, d, s);
+        return first < plain ? s : 1;
+    }
+    if (p.waves != 4) return 1;
     const int64_t last_rows = N - (ceil_div(N, p.block_q) - 1) * p.block_q;
     if (last_rows > 32 || ceil_div(Nk, p.block_k) < 32) return 1;
     if (p.grid > (int64_t)fwd_per_cu(d, p.block_k, p.waves) * kCus) return 1;
@@ -278,6 +363,14 @@ inline bool apply_tile_override(fa_plan* p, const char* tile, int64_t B, int64_t
     return true;
 }
 
+// Sets the plan's last-block key split for Nk keys per head, and the grid it launches (the
+// 8-wave launch of a tail-first plan covers the full 256-row blocks only).
+inline void finalize_tail(fa_plan* p, int dtype, int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d,
+                          int causal) {
+    p->tail_kv_splits = fwd_tail_kv_splits(*p, dtype, B, H, N, Nk, d, causal);
+    p->grid = B * H * (p->waves == 8 && p->tail_kv_splits > 1 ? N / p->block_q : ceil_div(N, p->block_q));
+}
+
 }  // namespace fa
 
 // Launchers implemented in fa_fwd_kernel.hip.  Return 0 on success or the
@@ -285,7 +378,7 @@ inline bool apply_tile_override(fa_plan* p, const char* tile, int64_t B, int64_t
 int fa_launch_fwd(const fa::FwdArgs& a, const fa_plan& plan, int dtype, int d, int causal,
                   hipStream_t stream);
 // Split-KV forward (bf16/fp16, non-causal): a.splits > 1, a.o_part / a.lse_part set;
-// launches the partial kernel and the merge.  rows = B*H*N.
-int fa_launch_fwd_splitkv(const fa::FwdArgs& a, int64_t rows, int dtype, int d, hipStream_t stream);
+// launches the partial kernel over a's grid and then the merge of m's rows.
+int fa_launch_fwd_splitkv(const fa::FwdArgs& a, const fa::MergeArgs& m, int dtype, int d, hipStream_t stream);
 // rows = B*H*N.  Launches the preprocess, dQ and dK/dV kernels in stream order.
 int fa_launch_bwd(const fa::BwdArgs& a, int64_t rows, int dtype, int d, int causal, hipStream_t stream);

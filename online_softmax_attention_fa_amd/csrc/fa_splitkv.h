@@ -8,8 +8,6 @@ namespace fa {
 
 // Split-KV (key ranges processed by separate workgroups, then merged by their LSE).
 constexpr int kMaxKvSplits = 64;
-// Key tile of the split-KV path (the 4-wave tile-loop kernel's Bc).
-inline int splitkv_block_k(int64_t d) { return d == 128 ? 64 : 128; }
 // Workspace of fa_fwd_splitkv: partial O (fp32) and partial LSE per split, 256-byte aligned.
 inline size_t splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int splits) {
     if (splits <= 1) return 0;

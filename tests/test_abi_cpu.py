@@ -162,39 +162,71 @@ def test_plan_respects_lds_and_covers_rows(lib, dtype, d):
         assert p["waves"] * 64 <= 1024
         assert p["block_q"] * p["wave_kv_splits"] == p["waves"] * p["rows_per_wave"]
         assert p["rows_per_wave"] % 32 == 0 and p["block_k"] % 32 == 0
-        assert p["grid"] == B * H * -(-N // p["block_q"])
+        tail_first = p["waves"] == 8 and p["tail_kv_splits"] > 1
+        assert p["grid"] == B * H * (N // p["block_q"] if tail_first else -(-N // p["block_q"]))
+        assert not tail_first or 1 <= N % 256 <= 32
         assert p["kv_splits"] >= 1
 
 
-def test_plan_splits_the_keys_of_a_short_last_block_only_on_grids_resident_at_once(lib):
-    # The last query block's waves share its <= 32 rows and split the key tiles four ways on
-    # non-causal 4-wave plans whose grid fits in one round, with at least 32 key tiles.
+def test_plan_splits_the_keys_of_a_short_last_block_only_on_grids_resident_at_once(lib, monkeypatch):
+    # On the 4-wave plans (pinned here through FA_TILE) the last query block's waves share its
+    # <= 32 rows and split the key tiles four ways when the grid fits in one round, with at
+    # least 32 key tiles.
     def tail(B, H, N, d, dtype=fa.FA_BF16, causal=False):
         return fa.fa_fwd_plan(B, H, N, d, dtype, causal=causal)["tail_kv_splits"]
 
+    monkeypatch.setenv("FA_TILE", "128,32,4")
     assert tail(2, 8, 4097, 128) == 4            # 528 workgroups at three per CU: one round
     assert tail(2, 8, 4097, 128, fa.FA_F16) == 4
     assert tail(2, 8, 4128, 128) == 4            # 32 rows in the last block
-    assert tail(2, 8, 4097, 64) == 4             # 64-key tiles at three per CU
     assert tail(2, 4, 8193, 128) == 4
     assert tail(2, 8, 4129, 128) == 1            # 33 rows: two waves hold rows
     assert tail(4, 8, 4097, 128) == 1            # 1056 workgroups: more than one round
     assert tail(2, 8, 4097, 128, causal=True) == 1
-    assert tail(1, 2, 257, 128) == 1             # 5 key tiles: too few to share
-    assert tail(4, 32, 16384, 128) == 1          # 8-wave plan, no ragged block
+    assert tail(1, 2, 257, 128) == 1             # 9 key tiles: too few to share
+    monkeypatch.setenv("FA_TILE", "128,64,4")
+    assert tail(2, 8, 4097, 64) == 4             # 64-key tiles at three per CU
+    monkeypatch.delenv("FA_TILE")
     assert tail(1, 1, 4097, 64, fa.FA_F32) == 1
     assert tail(0, 8, 4097, 128) == 0            # empty problem: the plan is all zeros
-    for B, H, N in [(1, 1, 1), (1, 1, 256), (4, 16, 2048), (2, 8, 4097), (4, 32, 16384)]:
-        assert fa.fa_fwd_plan(B, H, N, 128, fa.FA_BF16)["tail_kv_splits"] in (1, 4)
+    assert tail(2, 8, 4129, 128) == 1            # the chooser's 4-wave plan, 33 last rows
+
+
+def test_plan_computes_the_last_rows_first_on_eight_wave_grids(lib):
+    # N = 256 k + r, 1 <= r <= 32, where the 8-wave grid of full blocks costs less than the one
+    # with the short last blocks: the r rows of every head go ahead of the main launch on
+    # tail_kv_splits workgroups per head (about 256 in all, at most 16 key tiles per range),
+    # and the main grid covers the full blocks only.
+    def plan(B, H, N, d=128, dtype=fa.FA_BF16, causal=False):
+        p = fa.fa_fwd_plan(B, H, N, d, dtype, causal=causal)
+        return p["waves"], p["grid"], p["tail_kv_splits"]
+
+    assert plan(2, 8, 4097) == (8, 256, 16)      # one round of 256 full blocks
+    assert plan(2, 8, 4097, dtype=fa.FA_F16) == (8, 256, 16)
+    assert plan(2, 8, 4097, d=64) == (8, 256, 16)
+    assert plan(2, 8, 4128) == (8, 256, 16)      # 32 last rows
+    assert plan(2, 4, 8193) == (8, 256, 32)      # 129 key tiles of 64: 16 per range at most
+    assert plan(4, 8, 4097) == (8, 512, 8)       # two rounds
+    assert plan(8, 8, 4097) == (8, 1024, 5)      # four rounds; 65 key tiles, at most 16 per range
+    assert plan(2, 8, 16385) == (8, 1024, 17)
+    assert plan(4, 16, 2049) == (8, 512, 4)
+    assert plan(2, 8, 4129)[2] == 1              # 33 last rows
+    assert plan(3, 8, 4097) == (8, 408, 1)       # the last round has room for the short blocks
+    assert plan(1, 8, 4097) == (8, 136, 1)       # under one round: likewise
+    assert plan(4, 32, 16384)[2] == 1            # no short block
+    assert plan(16, 64, 2049)[0] == 4            # 1024 heads: the second pass over K and V costs more
+    assert plan(8, 16, 2049)[0] == 4
+    assert plan(2, 8, 4097, causal=True)[2] == 1
+    assert plan(2, 8, 4097, dtype=fa.FA_F32)[2] == 1
 
 
 def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_short_heads(lib):
     # 528 workgroups of 128 rows: two per CU leave a nearly empty second round, three per
     # CU (32-key tiles) fit them in one; causal grids and full rounds keep 64-key tiles
-    p = fa.fa_fwd_plan(2, 8, 4097, 128, fa.FA_BF16)
+    p = fa.fa_fwd_plan(2, 8, 4129, 128, fa.FA_BF16)
     assert (p["waves"], p["block_k"], p["grid"]) == (4, 32, 528)
     assert fa.fa_fwd_plan(5, 8, 2048, 128, fa.FA_F16)["block_k"] == 32
-    assert fa.fa_fwd_plan(2, 8, 4097, 128, fa.FA_BF16, causal=True)["block_k"] == 64
+    assert fa.fa_fwd_plan(2, 8, 4129, 128, fa.FA_BF16, causal=True)["block_k"] == 64
     # short sequences with two or more 128-row workgroups per CU also take 32-key tiles
     # (latency-bound: a third resident workgroup overlaps copies with compute); a small
     # grid, or a causal one, keeps 64-key tiles
@@ -212,7 +244,7 @@ def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_sh
     p = fa.fa_fwd_plan(3, 6, 3000, 128, fa.FA_BF16)
     assert (p["waves"], p["block_k"], p["grid"]) == (8, 128, 216)
     # d = 64, 528 blocks of 128 rows: three per CU in one round (as at d = 128)
-    p = fa.fa_fwd_plan(2, 8, 4097, 64, fa.FA_BF16)
+    p = fa.fa_fwd_plan(2, 8, 4129, 64, fa.FA_BF16)
     assert (p["waves"], p["block_k"], p["grid"]) == (4, 64, 528)
 
 
@@ -222,10 +254,18 @@ def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_sh
     (3, 8, 4097, 128, (8, 128)),     # 408 blocks of 256: 218 us; 4 waves 233-238 us
     (2, 8, 2049, 128, (8, 128)),     # 144 blocks of 256: 58 us; 4 waves 62-63 us
     (2, 8, 4000, 128, (8, 128)),     # 256 blocks of 256: 125 us; 4 waves 133-134 us
-    (2, 8, 4097, 128, (4, 32)),      # 528 blocks of 128 at three per CU: 176 us; others 190-201 us
-    (4, 8, 4097, 128, (4, 32)),      # 1056 blocks of 128: 288 us; others 304-307 us
-    (1, 16, 4097, 128, (4, 32)),     # 528 blocks of 128: 166 us; others 183-184 us
-    (2, 16, 4097, 64, (4, 64)),      # d = 64, 1056 blocks: 180 us; 8 waves 196 us, 2 per CU 187 us
+    # last rows first, then 256 (512) full blocks of 256 rows: 139 us against 151 us for three
+    # 4-wave workgroups per CU with the last block's key split (265 against 293 us; 139 against
+    # 150 us; d = 64 163 against 183 us)
+    (2, 8, 4097, 128, (8, 128)),
+    (4, 8, 4097, 128, (8, 128)),
+    (1, 16, 4097, 128, (8, 128)),
+    (2, 16, 4097, 64, (8, 128)),
+    (2, 8, 4129, 128, (4, 32)),      # 33 last rows: 528 blocks of 128 at three per CU
+    (8, 8, 4097, 128, (8, 128)),     # last rows first: 505 us; 4 waves 527 us, 8 waves with short blocks 527 us
+    (2, 8, 16385, 128, (8, 128)),    # last rows first: 1.88 ms; 2.05 and 2.07 ms
+    (16, 64, 2049, 128, (4, 32)),    # 1024 heads: 2.13 ms; 8 waves 2.27 ms, last rows first 2.33 ms
+    (8, 16, 2049, 128, (4, 32)),     # 273 us; last rows first 285 us, 8 waves 290 us
     (1, 8, 4096, 128, (4, 64)),      # 256 blocks of 128, one per CU: 80 us; 8 waves 100 us
     (4, 16, 2048, 64, (8, 128)),     # 512 blocks of 256 (ping-pong): 84 us; 4 waves 86-87 us
 ])

@@ -283,7 +283,7 @@ def test_eight_wave_plan_sampled(gpu_lib, monkeypatch, dtype, d, N, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("B,H,N", [(5, 8, 2001), (2, 8, 4097)])
+@pytest.mark.parametrize("B,H,N", [(5, 8, 2001), (2, 8, 4129)])
 def test_three_per_cu_plan_sampled(gpu_lib, dtype, B, H, N):
     # grids just over one round of two 128-row workgroups per CU run on the 32-key-tile
     # kernel at three per CU (non-causal); ragged last query block and key tile
@@ -305,6 +305,72 @@ def test_three_per_cu_plan_sampled(gpu_lib, dtype, B, H, N):
         Lg = lse[b, h].index_select(0, rr).cpu().numpy().astype(np.float64)
         O_ref, L_ref = attention_rows(q[b, h], k[b, h], v[b, h], scale_of(d), rows)
         compare(Og, Lg, O_ref, L_ref, dtype, f"B{B} H{H} N={N} {dtype} b{b} h{h}")
+
+
+TAIL_FIRST = [
+    # (B, H, N, d, dtype): 8-wave plans whose last N % 256 rows run ahead of the main launch
+    (2, 8, 4097, 128, "bf16"),    # one round of 256 full blocks, one last row per head
+    (2, 8, 4097, 64, "fp16"),     # d = 64: the ping-pong main launch
+    (2, 4, 8193, 128, "fp16"),
+    (2, 8, 4128, 128, "bf16"),    # 32 last rows
+    (2, 8, 4113, 64, "bf16"),     # 17 last rows
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype", TAIL_FIRST, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}{c[4]}" for c in TAIL_FIRST])
+def test_tail_first(gpu_lib, B, H, N, d, dtype):
+    # The split-KV launch computes the last rows of every head into partials parked in the
+    # head's first O rows, the merge writes those rows' O and LSE, and the 8-wave launch then
+    # overwrites the parked partials with the full blocks' outputs: every row equals the oracle.
+    plan = gpu_lib.fa_fwd_plan(B, H, N, d, wl_dtype_code(dtype))
+    assert plan["waves"] == 8 and plan["tail_kv_splits"] > 1 and plan["grid"] == B * H * (N // 256), plan
+    q, k, v = _random_qkv(B, H, N, d, dtype, seed=N * 7 + d)
+    O, L = run_fwd(gpu_lib, q, k, v, dtype)
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(d))
+    compare(O, L, O_ref, L_ref, dtype, f"tail first B{B} H{H} N{N} d{d} {dtype}")
+
+
+def test_tail_first_non_finite(gpu_lib):
+    # NaN in a last row's query stays in that row; a NaN key in the last split's range reaches
+    # every row, the last rows through the merge; a NaN value row reaches every output row but
+    # no LSE.
+    B, H, N, d, dtype = 2, 8, 4097, 128, "bf16"
+    assert gpu_lib.fa_fwd_plan(B, H, N, d, wl_dtype_code(dtype))["tail_kv_splits"] > 1
+    q, k, v = _random_qkv(B, H, N, d, dtype, seed=99)
+    qn = q.copy(); qn[1, 5, N - 1, 7] = np.nan
+    O, L = run_fwd(gpu_lib, qn, k, v, dtype)
+    bad_o, bad_l = ~np.isfinite(O), ~np.isfinite(L)
+    assert bad_o[1, 5, N - 1].all() and bad_l[1, 5, N - 1]
+    bad_o[1, 5, N - 1] = False; bad_l[1, 5, N - 1] = False
+    assert not bad_o.any() and not bad_l.any(), "a NaN query row leaked"
+    kn = k.copy(); kn[0, 2, N - 2, 3] = np.nan
+    O, L = run_fwd(gpu_lib, q, kn, v, dtype)
+    assert (~np.isfinite(O[0, 2])).all(axis=1).all() and (~np.isfinite(L[0, 2])).all()
+    assert np.isfinite(O[0, 3]).all() and np.isfinite(L[1]).all(), "a NaN key leaked to another head"
+    vn = v.copy(); vn[1, 1, 10, 4] = np.nan
+    O, L = run_fwd(gpu_lib, q, k, vn, dtype)
+    assert (~np.isfinite(O[1, 1, :, 4])).all() and np.isfinite(L).all()
+
+
+def test_tail_first_not_taken_when_o_overlaps_an_input(gpu_lib, capfd, monkeypatch):
+    # O written over Q (each block reads its own Q rows before it writes them): the parked
+    # partials would overwrite queries not read yet, so the call takes the 8-wave grid with
+    # its short last block instead, and the result still equals the oracle.
+    import torch
+
+    B, H, N, d, dtype = 2, 8, 4097, 128, "bf16"
+    q, k, v = _random_qkv(B, H, N, d, dtype, seed=5)
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(d))
+    monkeypatch.setenv("FA_LOG", "1")
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    o, lse = gpu_lib.fa_fwd(tq, tk, tv)
+    torch.cuda.synchronize()
+    assert "rows first" in capfd.readouterr().err
+    compare(to_host(o), lse.cpu().numpy().astype(np.float64), O_ref, L_ref, dtype, "separate O")
+    o2, lse2 = gpu_lib.fa_fwd(tq, tk, tv, o=tq)
+    torch.cuda.synchronize()
+    assert "rows first" not in capfd.readouterr().err
+    compare(to_host(o2), lse2.cpu().numpy().astype(np.float64), O_ref, L_ref, dtype, "O over Q")
 
 
 def wl_dtype_code(dtype):

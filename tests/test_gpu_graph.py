@@ -115,17 +115,19 @@ def test_fp8_and_causal_in_one_graph(gpu_lib):
 
 
 def test_ping_pong_and_short_head_forwards_in_one_graph(gpu_lib, monkeypatch):
-    """The d = 64 ping-pong schedule (8-wave plan, three stages; pinned through FA_TILE) and
-    the three-per-CU short-head plans (d = 64 and d = 128) captured together; every replay
-    must reproduce the eager results bit for bit."""
+    """The d = 64 ping-pong schedule (8-wave plan, three stages; pinned through FA_TILE), the
+    three-per-CU short-head plans (d = 64 and d = 128) and a tail-first forward (its split-KV
+    and merge launches ahead of the 8-wave one, partials parked in O) captured together;
+    every replay must reproduce the eager results bit for bit, with O and the LSE filled with
+    NaN before each."""
     import os
 
     import torch
 
     fa = gpu_lib
     gen = torch.Generator(device="cuda").manual_seed(37)
-    shapes = ((4, 16, 2100, 64), (16, 32, 300, 64), (16, 32, 300, 128))
-    tiles = ("256,128,8", "", "")     # the library reads FA_TILE at each call
+    shapes = ((4, 16, 2100, 64), (16, 32, 300, 64), (16, 32, 300, 128), (2, 8, 4097, 128))
+    tiles = ("256,128,8", "", "", "")     # the library reads FA_TILE at each call
     plans = []
     for sh, tile in zip(shapes, tiles):
         monkeypatch.setenv("FA_TILE", tile)
@@ -133,6 +135,7 @@ def test_ping_pong_and_short_head_forwards_in_one_graph(gpu_lib, monkeypatch):
     assert (plans[0]["waves"], plans[0]["block_k"]) == (8, 128)
     assert (plans[1]["waves"], plans[1]["block_k"]) == (4, 64)
     assert (plans[2]["waves"], plans[2]["block_k"]) == (4, 32)
+    assert (plans[3]["waves"], plans[3]["block_k"], plans[3]["tail_kv_splits"]) == (8, 128, 16)
     ins = [tuple(torch.randn(*sh, device="cuda", dtype=torch.bfloat16, generator=gen) for _ in range(3))
            for sh in shapes]
     outs = [(torch.empty_like(q), torch.empty(q.shape[:3], device="cuda", dtype=torch.float32)) for q, _, _ in ins]

@@ -66,6 +66,18 @@ def test_poisoned_forward_parity(poison_lib, monkeypatch, tile, d, dtype, causal
         compare(O, L, O_ref, L_ref, dtype, f"poison FA_TILE={tile} d={d} {dtype} N={N} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_poisoned_tail_first_parity(gpu_lib, poison_lib, d):
+    # the last row of every head computed ahead of the 8-wave launch (split-KV workgroups
+    # over the head's key ranges, partials parked in O, merged), every stage poisoned
+    B, H, N, dtype = 2, 8, 4097, "bf16"
+    assert gpu_lib.fa_fwd_plan(B, H, N, d, gpu_lib.FA_BF16)["tail_kv_splits"] > 1
+    q, k, v = (wl.random_tensor((B, H, N, d), dtype, [N, d, 41, t]) for t in (1, 2, 3))
+    O, L = _fwd(poison_lib, *(to_device(x, dtype) for x in (q, k, v)), False)
+    O_ref, L_ref = _oracle(q, k, v, d, False)
+    compare(O, L, O_ref, L_ref, dtype, f"poison tail first d={d}")
+
+
 def test_poisoned_splitkv_parity(poison_lib):
     import torch
 
