@@ -238,6 +238,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
 #pragma unroll
         for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
     float m = -INFINITY, lsum = 0.f, lrnd = 0.f;
+    bool max_first = false;   // the next tile takes its maximum before forming P
 
     int n_tiles = (NK + BC - 1) / BC;
     if (CAUSAL) n_tiles = min(n_tiles, (min(N, (qblk + 1) * BR) + BC - 1) / BC);
@@ -329,8 +330,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         };
         // The workgroup's first tile meets m = -inf, which would fail the test anyway: it takes
         // its own maximum at once.  (NaN, from -inf scores against m = -inf, fails the test.)
+        // Non-causal bf16: after a tile whose maximum jumped, the next one does the same; on
+        // heads whose maxima keep jumping (one-hot or large scores) most first attempts would
+        // fail.  (The causal and fp16 kernels measured slower with it.)
+        constexpr bool kMaxFirst = !CAUSAL && !ONE_SUM;
         bool redo = true;
-        if (j != jfirst) {
+        if (j != jfirst && !(kMaxFirst && max_first)) {
             make_p(-m);
             redo = __builtin_amdgcn_ballot_w64(!((ONE_SUM ? racc0 + racc1 : acc0 + acc1) <= kMaxTileSum)) != 0;
         }
@@ -344,6 +349,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                     x1 = vmax3(x1, s[kb][t + 2], s[kb][t + 3]);
                 }
             const float xm = pair_max(__builtin_elementwise_maximum(x0, x1));
+            if constexpr (kMaxFirst) max_first = j != jfirst && __builtin_amdgcn_ballot_w64(xm * c > m + 12.f) != 0;
             const float mx = ONE_SUM ? xm * c : __builtin_fmaf(xm, c, a.m_headroom);
             const float mnew = fmaxf(m, mx);
             const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
