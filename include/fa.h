@@ -127,7 +127,9 @@ typedef struct {
  * LSE: [B,H,N] fp32 (natural log).  `scale` multiplies Q K^T (1/sqrt(d) for the
  * usual attention).  Supported: d in {64, 128}; dtype FA_BF16 / FA_F16 (matrix
  * products on bf16/fp16 MFMA with fp32 accumulation and fp32 softmax statistics)
- * or FA_F32 (fp32 MFMA throughout).  Any N >= 0 (tails are masked).
+ * or FA_F32 (fp32 MFMA throughout).  Any N >= 0 (tails are masked).  O may also hold
+ * intermediate values while the call's work runs (see fa_plan.tail_kv_splits): read it only
+ * after the stream has passed the call.  O may coincide with Q (computed in place).
  */
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
