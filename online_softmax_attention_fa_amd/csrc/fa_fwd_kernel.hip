@@ -239,6 +239,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
         for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
     float m = -INFINITY, lsum = 0.f, lrnd = 0.f;
     bool max_first = false;   // the next tile takes its maximum before forming P
+    // bf16 causal d = 64, 8 waves: the O divisor (the sum of P as rounded for the MFMA) comes
+    // from the matrix cores, as row 0 of one more 32-row block of O^T whose V^T operand is a
+    // row of ones (lanes 0 and 32 hold its keys) -- KS more MFMAs per tile on a pipe this
+    // VALU-bound kernel leaves two thirds idle, instead of 8 v_dot2 per 16 scores (3% faster
+    // at B4 H16 N4096; the ping-pong kernel measured no gain and keeps the v_dot2 sum).
+    constexpr bool kSumOnMfma = D == 64 && WAVES == 8 && !ONE_SUM && CAUSAL;
+    f32x16 osum;
+    u32x4 ones{0u, 0u, 0u, 0u};
+    if constexpr (kSumOnMfma) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) osum[t] = 0.f;
+        if (l32 == 0) ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    }
 
     int n_tiles = (NK + BC - 1) / BC;
     if (CAUSAL) n_tiles = min(n_tiles, (min(N, (qblk + 1) * BR) + BC - 1) / BC);
@@ -321,8 +334,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         f[w] = Elt<T>::pack2(p[8 * half + 2 * w], p[8 * half + 2 * w + 1]);
-                        if (w & 1) racc1 = Elt<T>::sum2(f[w], racc1);
-                        else racc0 = Elt<T>::sum2(f[w], racc0);
+                        if constexpr (!kSumOnMfma) {
+                            if (w & 1) racc1 = Elt<T>::sum2(f[w], racc1);
+                            else racc0 = Elt<T>::sum2(f[w], racc0);
+                        }
                     }
                     pf[2 * kb + half] = f;
                 }
@@ -356,6 +371,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
             m = mnew;
             lsum *= alpha;
             lrnd *= alpha;
+            if constexpr (kSumOnMfma) osum[0] *= alpha;   // (its other elements stay 0)
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -363,7 +379,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
             make_p(-m);
         }
         if constexpr (!ONE_SUM) lsum += acc0 + acc1;
-        lrnd += racc0 + racc1;
+        if constexpr (!kSumOnMfma) lrnd += racc0 + racc1;
     };
     auto qk_soft = [&](int j, const lds_u8* sbase) __attribute__((always_inline)) {
         qk_soft_with(j, [&](int i) { return lds_read16(sbase, koff[i % DS] + (i / DS) * 32 * RB); }, t0);
@@ -389,6 +405,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
                 if (i + VPF < NPV) vf[(i + VPF) % (VPF + 1)] = vread(i + VPF);
                 o[i / KS] = Elt<T>::mma(vf[i % (VPF + 1)], pf[i % KS], o[i / KS]);
                 __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (kSumOnMfma) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) osum = Elt<T>::mma(ones, pf[ks], osum);
             }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -598,6 +618,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     }
 
     // ---- epilogue: O / l, LSE = (m + log2 l) ln 2
+    if constexpr (kSumOnMfma) lrnd = osum[0];   // lanes 0-31; 0 on lanes 32-63 (row 4)
     const float lr = pair_sum(lrnd);
     const float lt = ONE_SUM ? lr : pair_sum(lsum);
     const float inv = 1.0f / lr;
