@@ -373,6 +373,34 @@ def test_tail_first_not_taken_when_o_overlaps_an_input(gpu_lib, capfd, monkeypat
     compare(to_host(o2), lse2.cpu().numpy().astype(np.float64), O_ref, L_ref, dtype, "O over Q")
 
 
+IN_PLACE = [
+    # (B, H, N, d, dtype, causal, FA_TILE): O written over Q on each kind of plan
+    (2, 8, 4129, 128, "bf16", False, ""),           # 4 waves, 32-key tiles, three per CU
+    (1, 2, 1153, 128, "bf16", False, "128,32,4"),   # the last block's waves split its keys
+    (2, 4, 2100, 64, "fp16", False, "256,128,8"),   # ping-pong
+    (1, 4, 1500, 128, "bf16", True, ""),            # causal
+    (1, 2, 300, 64, "fp32", False, ""),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal,tile", IN_PLACE,
+                         ids=[f"{c[4]}-N{c[2]}-d{c[3]}{'-causal' if c[5] else ''}{'-' + c[6] if c[6] else ''}" for c in IN_PLACE])
+def test_in_place_over_q(gpu_lib, monkeypatch, B, H, N, d, dtype, causal, tile):
+    # Every workgroup reads its own query rows before it writes their outputs, so O may be
+    # Q's memory (fa.h); the result equals the oracle's on the original queries.
+    import torch
+
+    if tile:
+        monkeypatch.setenv("FA_TILE", tile)
+    q, k, v = _random_qkv(B, H, N, d, dtype, seed=N + d + 3)
+    O_ref, L_ref = _oracle_full(q, k, v, scale_of(d), causal=causal)
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    o, lse = gpu_lib.fa_fwd(tq, tk, tv, o=tq, causal=causal)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == tq.data_ptr()
+    compare(to_host(o), lse.cpu().numpy().astype(np.float64), O_ref, L_ref, dtype, f"in place {dtype} N={N}")
+
+
 def wl_dtype_code(dtype):
     import online_softmax_attention_fa_amd as fa
 
