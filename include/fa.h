@@ -117,8 +117,8 @@ typedef struct {
                             /*     8 waves ("tail first"): those rows are computed     */
                             /*     ahead of the main launch by tail_kv_splits          */
                             /*     workgroups per head, their partials parked in the   */
-                            /*     head's first O rows and merged; the main launch     */
-                            /*     then covers the full blocks (not used when O        */
+                            /*     head's first O rows; the main launch covers the     */
+                            /*     full blocks and merges them first (not used when O  */
                             /*     overlaps Q, K, V or LSE)                            */
 } fa_plan;
 

@@ -174,8 +174,9 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
     a.o_part = nullptr;
     a.lse_part = nullptr;
     if (tail_first) {
-        // the last r rows of every head: split-KV partials parked in the head's first O rows,
-        // merged into its rows n_main .. N - 1, ahead of the main launch that overwrites them
+        // the last r rows of every head: split-KV partials parked in the head's first O rows;
+        // the main launch's first block of each head merges them into its rows n_main .. N - 1
+        // before its own outputs overwrite them
         const int S = plan.tail_kv_splits;
         const int64_t r = N - n_main, tiles = fa::ceil_div(N, fa::splitkv_block_k(d));
         fa::FwdArgs t = a;
@@ -190,21 +191,16 @@ fa_status fwd_common(const void* Q, const void* K, const void* V, void* O, float
         t.po_split = r * d;
         t.pl_split = r;
         t.part_row0 = (int)n_main;
-        fa::MergeArgs m;
-        m.o_part = t.o_part;
-        m.lse_part = t.lse_part;
-        m.o = O;
-        m.lse = LSE;
-        m.rows = B * H * r;
-        m.rows_per_head = (int)r;
-        m.splits = S;
-        m.po_head = t.po_head;
-        m.po_split = t.po_split;
-        m.pl_head = t.pl_head;
-        m.pl_split = t.pl_split;
-        m.out_head = N;
-        m.out_row0 = (int)n_main;
+        fa::MergeArgs m{};   // no rows: no merge launch
         if (fa_launch_fwd_splitkv(t, m, dtype, (int)d, stream) != 0) return FA_ERR_LAUNCH;
+        a.splits = S;
+        a.o_part = t.o_part;
+        a.lse_part = t.lse_part;
+        a.po_head = t.po_head;
+        a.po_split = t.po_split;
+        a.pl_head = t.pl_head;
+        a.pl_split = t.pl_split;
+        a.part_row0 = t.part_row0;
     }
     const int e = fa_launch_fwd(a, plan, dtype, (int)d, causal, stream);
     return e == 0 ? FA_OK : FA_ERR_LAUNCH;

@@ -62,6 +62,65 @@ namespace fa {
 // so if lane r of the group addresses V[k0 + r/4][d0 + 4(r%4) .. +3], lane c gets
 // V[k0 + e][d0 + c] for e = 0..3: four keys of its own column.
 
+// Merges S normalised partials (O_s, LSE_s) of one row by their log-sum-exp, the two-block
+// merge of "FlashAttention 硬件感知计算剖析" (section 二) generalised to S parts:
+//     LSE = ln sum_s e^{LSE_s},   O = sum_s e^{LSE_s - LSE} O_s.
+// The calling lane owns dims 8 part .. 8 part + 7 (two 16-byte loads per partial); partial s
+// of the row sits at o_part + s * po_split (D floats) and lse_part[s * pl_split].  The parts
+// are taken eight at a time, their loads issued together, and folded in with a running
+// maximum (the same merge applied chunk by chunk), so a row costs one pass over them.  The
+// lane writes its 8 dims of O; lse (if not null) gets the row's LSE.
+template <typename T, int D>
+__device__ __forceinline__ void merge_partials(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+                                               int64_t po_split, int64_t pl_split, int splits, int part,
+                                               T* __restrict__ o_row, float* __restrict__ lse) {
+    constexpr int CH = 8;
+    float mx = -INFINITY, den = 0.f;
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += CH) {
+        float l[CH];
+        f32x4 x0[CH], x1[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            l[i] = -INFINITY;
+            x0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            x1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (s0 + i < splits) {
+                const int64_t s = s0 + i;
+                l[i] = lse_part[s * pl_split];
+                x0[i] = *reinterpret_cast<const f32x4*>(o_part + s * po_split + part * 8);
+                x1[i] = *reinterpret_cast<const f32x4*>(o_part + s * po_split + part * 8 + 4);
+            }
+        }
+        float cm = mx;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) cm = fmaxf(cm, l[i]);
+        if (cm == -INFINITY) continue;   // only empty key ranges so far (LSE_s = -inf, O_s = 0)
+        const float r = __expf(mx - cm);   // 0 while mx = -inf
+        den *= r;
+        a0 *= r;
+        a1 *= r;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const float w = __expf(l[i] - cm);
+            den += w;
+            a0 += w * x0[i];
+            a1 += w * x1[i];
+        }
+        mx = cm;
+    }
+    const float inv = 1.f / den;
+    a0 *= inv;
+    a1 *= inv;
+    u32x4 out;
+    out[0] = Elt<T>::pack2(a0[0], a0[1]);
+    out[1] = Elt<T>::pack2(a0[2], a0[3]);
+    out[2] = Elt<T>::pack2(a1[0], a1[1]);
+    out[3] = Elt<T>::pack2(a1[2], a1[3]);
+    *reinterpret_cast<u32x4*>(o_row + part * 8) = out;
+    if (lse) *lse = mx + __logf(den);
+}
+
 template <typename T, int D, int BC, int WAVES, bool CAUSAL, bool SPLIT = false, bool PP = false, bool TAIL = false>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 2) : 1) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource types exist only in the device pass
@@ -80,7 +139,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     static_assert(LOADS >= 1 && TILE % (NT * 16) == 0, "tile must be whole 4 KiB blocks");
     static_assert(!(SPLIT && CAUSAL), "split-KV is non-causal");
     static_assert(!PP || (WAVES == 8 && !CAUSAL && !SPLIT), "ping-pong: 8 waves, non-causal");
-    static_assert(!TAIL || (WAVES == 4 && !CAUSAL && !SPLIT), "last-block key split: 4 waves, non-causal");
+    // TAIL: on 4 waves the last-block key split; on 8 waves the merge of the last rows
+    // computed ahead of the launch (tail first)
+    static_assert(!TAIL || (!CAUSAL && !SPLIT), "last-block variants: non-causal");
 
     // A stage is a K tile and a V tile.  Each stage is an array of its own, so the compiler
     // can prove that the copies into one stage do not alias the reads of the other and adds no
@@ -142,13 +203,28 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     T* __restrict__ Oh = reinterpret_cast<T*>(a.o) + head;
     float* __restrict__ Lh = a.lse + (int64_t)bh * N;
 
+    // Tail first (the 8-wave TAIL variants): the last rows of each head (from row part_row0
+    // on) were computed ahead of this launch into partials parked in the head's first O
+    // rows; the head's first block merges them into those rows' O and LSE before its own
+    // outputs overwrite the partials (its epilogue comes after many tile barriers, by which
+    // time every merge load of the workgroup has returned).
+    if constexpr (TAIL && WAVES == 8) {
+        if (qblk == 0) {
+            const int i = tid / (D / 8), part = tid % (D / 8);
+            if (i < N - a.part_row0)
+                merge_partials<T, D>(a.o_part + bh * a.po_head + (int64_t)i * D, a.lse_part + bh * a.pl_head + i,
+                                     a.po_split, a.pl_split, a.splits, part, Oh + (int64_t)(a.part_row0 + i) * D,
+                                     part == 0 ? Lh + a.part_row0 + i : nullptr);
+        }
+    }
+
     // TAIL: a block whose rows all fit in its first wave (the one-row last block when N is one
     // more than a multiple of Br; one-query decoding) would leave its other waves idle while
     // the first sweeps every key.  There every wave (four: the two stages hold four V tiles)
     // takes the first wave's rows and a quarter of the key tiles, and the four partial results
     // are merged through LDS at the end.  A variant of its own, launched where it measured
     // faster, so the others keep their code.
-    constexpr bool kTailSplit = TAIL;
+    constexpr bool kTailSplit = TAIL && WAVES == 4;
     const bool tail_split = kTailSplit && N - qblk * BR <= QPW;
     const int q_wave = qblk * BR + (tail_split ? 0 : wave * QPW);   // first query row of this wave
     const int query = q_wave + l32;              // the query this lane's columns belong to
@@ -699,75 +775,24 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
 
 // ---------------------------------------------------------- split-KV merge ---
 //
-// Combines the normalised partials of the key ranges by their log-sum-exp, the two-block
-// merge of "FlashAttention 硬件感知计算剖析" (section 二) generalised to S parts:
-//     LSE = ln sum_s e^{LSE_s},   O = sum_s e^{LSE_s - LSE} O_s.
-// D / 8 lanes per row, 8 dims (two 16-byte loads per partial) each.  The parts are taken eight
-// at a time, their loads issued together, and folded in with a running maximum (the same
-// merge applied chunk by chunk), so a row costs one pass over its partials.
+// One row per D / 8 lanes, each lane 8 dims: merge_partials above.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void splitkv_merge_kernel(MergeArgs a) {
-    constexpr int LPR = D / 8, RPB = 256 / LPR, CH = 8;
+    constexpr int LPR = D / 8, RPB = 256 / LPR;
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
     if (row >= a.rows) return;
     const int64_t bh = row / a.rows_per_head, i = row - bh * a.rows_per_head;
-    const float* __restrict__ o_part = a.o_part + bh * a.po_head + i * D;
-    const float* __restrict__ lse_part = a.lse_part + bh * a.pl_head + i;
-    const int splits = a.splits;
-    float mx = -INFINITY, den = 0.f;
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < splits; s0 += CH) {
-        float l[CH];
-        f32x4 x0[CH], x1[CH];
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            l[i] = -INFINITY;
-            x0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            x1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (s0 + i < splits) {
-                const int64_t s = s0 + i;
-                l[i] = lse_part[s * a.pl_split];
-                x0[i] = *reinterpret_cast<const f32x4*>(o_part + s * a.po_split + part * 8);
-                x1[i] = *reinterpret_cast<const f32x4*>(o_part + s * a.po_split + part * 8 + 4);
-            }
-        }
-        float cm = mx;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) cm = fmaxf(cm, l[i]);
-        if (cm == -INFINITY) continue;   // only empty key ranges so far (LSE_s = -inf, O_s = 0)
-        const float r = __expf(mx - cm);   // 0 while mx = -inf
-        den *= r;
-        a0 *= r;
-        a1 *= r;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const float w = __expf(l[i] - cm);
-            den += w;
-            a0 += w * x0[i];
-            a1 += w * x1[i];
-        }
-        mx = cm;
-    }
-    const float lse = mx + __logf(den);
-    const float inv = 1.f / den;
-    a0 *= inv;
-    a1 *= inv;
-    u32x4 out;
-    out[0] = Elt<T>::pack2(a0[0], a0[1]);
-    out[1] = Elt<T>::pack2(a0[2], a0[3]);
-    out[2] = Elt<T>::pack2(a1[0], a1[1]);
-    out[3] = Elt<T>::pack2(a1[2], a1[3]);
     const int64_t orow = bh * a.out_head + a.out_row0 + i;
-    *reinterpret_cast<u32x4*>(reinterpret_cast<T*>(a.o) + orow * D + part * 8) = out;
-    if (part == 0) a.lse[orow] = lse;
+    merge_partials<T, D>(a.o_part + bh * a.po_head + i * D, a.lse_part + bh * a.pl_head + i, a.po_split, a.pl_split,
+                         a.splits, part, reinterpret_cast<T*>(a.o) + orow * D, part == 0 ? a.lse + orow : nullptr);
 }
 
 template <typename T, int D, int BC>
 static hipError_t launch_splitkv_t(const FwdArgs& a, const MergeArgs& m, hipStream_t st) {
     hipLaunchKernelGGL((fwd_kernel<T, D, BC, 4, false, true>), dim3((unsigned)a.n_blocks), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || m.rows == 0) return e;   // (no rows: the next launch merges them)
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((splitkv_merge_kernel<T, D>), dim3((unsigned)((m.rows + RPB - 1) / RPB)), dim3(256), 0, st, m);
     return hipGetLastError();
@@ -958,17 +983,15 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(FwdArgs a) {
 
 // ------------------------------------------------------------------ dispatch ---
 
-// tail: the plan's last-block key split on a 4-wave plan (its waves share the block's rows)
+// tail: the plan's last-block variant -- on 4 waves the key split (its waves share the
+// block's rows), on 8 waves the merge of the last rows computed ahead (tail first)
 template <typename T, int D, int BC, int WAVES>
 static hipError_t launch_t(const FwdArgs& a, int causal, bool tail, hipStream_t st) {
     const dim3 grid((unsigned)a.n_blocks), block(64 * WAVES);
     if (causal) {
         hipLaunchKernelGGL((fwd_kernel<T, D, BC, WAVES, true>), grid, block, 0, st, a);
     } else if (tail) {
-        if constexpr (WAVES == 4)
-            hipLaunchKernelGGL((fwd_kernel<T, D, BC, WAVES, false, false, false, true>), grid, block, 0, st, a);
-        else
-            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((fwd_kernel<T, D, BC, WAVES, false, false, false, true>), grid, block, 0, st, a);
     } else {
         hipLaunchKernelGGL((fwd_kernel<T, D, BC, WAVES, false>), grid, block, 0, st, a);
     }
@@ -978,14 +1001,16 @@ static hipError_t launch_t(const FwdArgs& a, int causal, bool tail, hipStream_t 
 // The compiled (d, Bc, waves) shapes; the chooser only emits these.
 template <typename T>
 static hipError_t launch_half(const FwdArgs& a, const fa_plan& p, int d, int causal, hipStream_t st) {
-    // (an 8-wave plan's tail_kv_splits is the tail-first split count: its last rows were
-    // computed by the split-KV launches ahead of this one)
-    const bool tail = p.waves == 4 && p.tail_kv_splits > 1;
+    const bool tail = p.tail_kv_splits > 1;
     if (d == 128 && p.block_k == 128 && p.waves == 8) return launch_t<T, 128, 128, 8>(a, causal, tail, st);
     if (d == 64 && p.block_k == 128 && p.waves == 8) {
         if (causal) return launch_t<T, 64, 128, 8>(a, causal, false, st);
         // non-causal d = 64 on the ping-pong schedule
-        hipLaunchKernelGGL((fwd_kernel<T, 64, 128, 8, false, false, true>), dim3((unsigned)a.n_blocks), dim3(512), 0, st, a);
+        if (tail)
+            hipLaunchKernelGGL((fwd_kernel<T, 64, 128, 8, false, false, true, true>), dim3((unsigned)a.n_blocks), dim3(512),
+                               0, st, a);
+        else
+            hipLaunchKernelGGL((fwd_kernel<T, 64, 128, 8, false, false, true>), dim3((unsigned)a.n_blocks), dim3(512), 0, st, a);
         return hipGetLastError();
     }
     if (d == 128 && p.block_k == 64 && p.waves == 4) return launch_t<T, 128, 64, 4>(a, causal, tail, st);

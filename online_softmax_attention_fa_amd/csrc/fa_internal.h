@@ -149,8 +149,9 @@ inline int splitkv_block_k(int64_t d) { return d == 128 ? 64 : 128; }
 // key alone: on a grid of whole rounds those blocks make a round of their own.  Instead the r
 // rows of every head are computed first by the split-KV kernel, S workgroups per head over
 // S key ranges, their normalised partials parked in the first rows of that head's O (which
-// the 8-wave launch overwrites later, in stream order), and merged into O and the LSE by the
-// merge kernel; the 8-wave launch then covers the k full blocks only.  S aims at 256
+// the 8-wave launch overwrites later, in stream order); the 8-wave launch then covers the k
+// full blocks, and the first block of each head merges those partials into the last rows'
+// O and LSE before its own outputs overwrite them.  S aims at 256
 // workgroups in all and at most 16 key tiles per range, within what the parked partials may
 // occupy: 4 S r (d + 1) bytes of the head's 256 k d 2 bytes of O.  Measured against the
 // plans before it (interleaved, N(0,1) inputs unless noted): B2 H8 N4097 d128 151.4 -> 139.2
