@@ -63,3 +63,41 @@ def test_random_shape_splitkv(gpu_lib, c):
     O_ref, L_ref = _oracle(q, k, v, scale, False)
     compare(to_host(o), lse.cpu().numpy().astype(np.float64), O_ref, L_ref, c["dtype"],
             _name(c) + f"-splits{c['splits']}")
+
+
+# Tail first: seeded grids of whole rounds of 256-row blocks plus 1..32 last rows per head
+# (the chooser computes those rows ahead of the 8-wave launch); checked on sampled rows that
+# include every last row and the first 256 rows of the head, where the partials are parked.
+_trng = np.random.default_rng(20261203)
+TAIL_CASES = []
+for i in range(8):
+    bh = int(_trng.choice([8, 16, 32]))
+    k = int(_trng.choice([256 // bh, 512 // bh]))   # whole rounds of 256 blocks
+    B = int(_trng.choice([1, 2]))
+    TAIL_CASES.append(dict(B=B, H=bh // B, N=256 * k + int(_trng.integers(1, 33)),
+                           d=int(_trng.choice([64, 128])), dtype=str(_trng.choice(["bf16", "fp16"])), seed=100 + i))
+
+
+@pytest.mark.parametrize("c", TAIL_CASES, ids=lambda c: "B{B}H{H}N{N}d{d}-{dtype}".format(**c))
+def test_random_tail_first(gpu_lib, c):
+    import torch
+
+    from oracle import attention_rows
+
+    B, H, N, d, dtype = c["B"], c["H"], c["N"], c["d"], c["dtype"]
+    code = {"bf16": gpu_lib.FA_BF16, "fp16": gpu_lib.FA_F16}[dtype]
+    plan = gpu_lib.fa_fwd_plan(B, H, N, d, code)
+    assert plan["waves"] == 8 and plan["tail_kv_splits"] > 1, plan
+    q, k, v = (wl.random_tensor((B, H, N, d), dtype, [c["seed"], 910 + t]) for t in (1, 2, 3))
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    o, lse = gpu_lib.fa_fwd(tq, tk, tv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(c["seed"])
+    n_main = N // 256 * 256
+    for b, h in ((0, 0), (B - 1, H - 1), (0, H // 2)):
+        rows = np.unique(np.concatenate([np.arange(0, 256, 7), np.arange(n_main, N), rng.choice(N, 24, replace=False)]))
+        rr = torch.from_numpy(rows).cuda()
+        Og = to_host(o[b, h].index_select(0, rr))
+        Lg = lse[b, h].index_select(0, rr).cpu().numpy().astype(np.float64)
+        O_ref, L_ref = attention_rows(q[b, h], k[b, h], v[b, h], scale_of(d), rows)
+        compare(Og, Lg, O_ref, L_ref, dtype, "tail first B{B}H{H}N{N}d{d}-{dtype} b{b} h{h}".format(b=b, h=h, **c))
