@@ -111,9 +111,10 @@ typedef struct {
     int32_t kv_splits;      /* >1: key range split across workgroups, then merged      */
     int32_t wave_kv_splits; /* >1: a workgroup's waves share its query rows and split  */
                             /*     the key tiles among themselves, merged in LDS       */
-    int32_t tail_kv_splits; /* >1: the last query block of each head (at most 32 rows) */
-                            /*     has its keys split.  4 waves: over the block's      */
-                            /*     waves, merged in LDS (whole grid resident at once). */
+    int32_t tail_kv_splits; /* >1: the last query block of each head (at most 32 rows; */
+                            /*     128 on 8 waves) has its keys split.  4 waves: over  */
+                            /*     the block's waves, merged in LDS (whole grid        */
+                            /*     resident at once).                                  */
                             /*     8 waves ("tail first"): those rows are computed     */
                             /*     ahead of the main launch by tail_kv_splits          */
                             /*     workgroups per head, their partials parked in the   */

@@ -210,8 +210,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? (BC * D == 32 * 128 ? 3 : 
     // time every merge load of the workgroup has returned).
     if constexpr (TAIL && WAVES == 8) {
         if (qblk == 0) {
-            const int i = tid / (D / 8), part = tid % (D / 8);
-            if (i < N - a.part_row0)
+            const int part = tid % (D / 8);
+            for (int i = tid / (D / 8); i < N - a.part_row0; i += NT / (D / 8))
                 merge_partials<T, D>(a.o_part + bh * a.po_head + (int64_t)i * D, a.lse_part + bh * a.pl_head + i,
                                      a.po_split, a.pl_split, a.splits, part, Oh + (int64_t)(a.part_row0 + i) * D,
                                      part == 0 ? Lh + a.part_row0 + i : nullptr);

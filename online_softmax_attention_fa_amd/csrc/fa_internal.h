@@ -144,9 +144,10 @@ inline double grid_time(int64_t w, double unit, int per_cu, const double* eff) {
 // Key tile of the split-KV path (the 4-wave tile-loop kernel's Bc).
 inline int splitkv_block_k(int64_t d) { return d == 128 ? 64 : 128; }
 
-// Last rows ahead of an 8-wave launch ("tail first").  When N = 256 k + r with 1 <= r <= 32,
-// the 8-wave grid's last block of each head holds r rows on its first wave, which sweeps every
-// key alone: on a grid of whole rounds those blocks make a round of their own.  Instead the r
+// Last rows ahead of an 8-wave launch ("tail first").  When N = 256 k + r with 1 <= r <= 128,
+// the 8-wave grid's last block of each head holds r rows on its first ceil(r / 32) waves, which
+// sweep every key while the others idle: on a grid of whole rounds those blocks make a round of
+// their own.  Instead the r
 // rows of every head are computed first by the split-KV kernel, S workgroups per head over
 // S key ranges, their normalised partials parked in the first rows of that head's O (which
 // the 8-wave launch overwrites later, in stream order); the 8-wave launch then covers the k
@@ -160,7 +161,7 @@ inline int splitkv_block_k(int64_t d) { return d == 128 ? 64 : 128; }
 // 505 us.  The tail rows read every head's K and V once more, so with many heads the
 // launches cost more than the round they save (B16 H64 N2049: 2.13 ms on the 4-wave plan,
 // 2.33 ms this way); tail_first_cost prices that.
-constexpr int kTailFirstMaxRows = 32;
+constexpr int kTailFirstMaxRows = 128;   // one 128-row block of the split-KV kernel per head
 inline int tail_first_splits(int64_t B, int64_t H, int64_t N, int64_t d) {
     const int64_t full = N / 256, r = N % 256;
     if (full <= 0 || r < 1 || r > kTailFirstMaxRows || B * H <= 0) return 1;

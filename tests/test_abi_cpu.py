@@ -189,11 +189,11 @@ def test_plan_splits_the_keys_of_a_short_last_block_only_on_grids_resident_at_on
     monkeypatch.delenv("FA_TILE")
     assert tail(1, 1, 4097, 64, fa.FA_F32) == 1
     assert tail(0, 8, 4097, 128) == 0            # empty problem: the plan is all zeros
-    assert tail(2, 8, 4129, 128) == 1            # the chooser's 4-wave plan, 33 last rows
+    assert tail(2, 8, 4300, 128) == 1            # the chooser's 4-wave plan, 76 last rows
 
 
 def test_plan_computes_the_last_rows_first_on_eight_wave_grids(lib):
-    # N = 256 k + r, 1 <= r <= 32, where the 8-wave grid of full blocks costs less than the one
+    # N = 256 k + r, 1 <= r <= 128, where the 8-wave grid of full blocks costs less than the one
     # with the short last blocks: the r rows of every head go ahead of the main launch on
     # tail_kv_splits workgroups per head (about 256 in all, at most 16 key tiles per range),
     # and the main grid covers the full blocks only.
@@ -210,7 +210,9 @@ def test_plan_computes_the_last_rows_first_on_eight_wave_grids(lib):
     assert plan(8, 8, 4097) == (8, 1024, 5)      # four rounds; 65 key tiles, at most 16 per range
     assert plan(2, 8, 16385) == (8, 1024, 17)
     assert plan(4, 16, 2049) == (8, 512, 4)
-    assert plan(2, 8, 4129)[2] == 1              # 33 last rows
+    assert plan(2, 8, 4129) == (8, 256, 16)      # 33 last rows
+    assert plan(2, 8, 4224) == (8, 256, 15)      # 128 last rows: 15 ranges fill the room in O
+    assert plan(2, 8, 4225)[0] == 4              # 129: more than one split-KV block per head
     assert plan(3, 8, 4097) == (8, 408, 1)       # the last round has room for the short blocks
     assert plan(1, 8, 4097) == (8, 136, 1)       # under one round: likewise
     assert plan(4, 32, 16384)[2] == 1            # no short block
@@ -223,10 +225,10 @@ def test_plan_computes_the_last_rows_first_on_eight_wave_grids(lib):
 def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_short_heads(lib):
     # 528 workgroups of 128 rows: two per CU leave a nearly empty second round, three per
     # CU (32-key tiles) fit them in one; causal grids and full rounds keep 64-key tiles
-    p = fa.fa_fwd_plan(2, 8, 4129, 128, fa.FA_BF16)
-    assert (p["waves"], p["block_k"], p["grid"]) == (4, 32, 528)
+    p = fa.fa_fwd_plan(2, 8, 4300, 128, fa.FA_BF16)
+    assert (p["waves"], p["block_k"], p["grid"]) == (4, 32, 544)
     assert fa.fa_fwd_plan(5, 8, 2048, 128, fa.FA_F16)["block_k"] == 32
-    assert fa.fa_fwd_plan(2, 8, 4129, 128, fa.FA_BF16, causal=True)["block_k"] == 64
+    assert fa.fa_fwd_plan(2, 8, 4300, 128, fa.FA_BF16, causal=True)["block_k"] == 64
     # short sequences with two or more 128-row workgroups per CU also take 32-key tiles
     # (latency-bound: a third resident workgroup overlaps copies with compute); a small
     # grid, or a causal one, keeps 64-key tiles
@@ -243,9 +245,9 @@ def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_sh
     # four-wave ones at up to two per CU
     p = fa.fa_fwd_plan(3, 6, 3000, 128, fa.FA_BF16)
     assert (p["waves"], p["block_k"], p["grid"]) == (8, 128, 216)
-    # d = 64, 528 blocks of 128 rows: three per CU in one round (as at d = 128)
-    p = fa.fa_fwd_plan(2, 8, 4129, 64, fa.FA_BF16)
-    assert (p["waves"], p["block_k"], p["grid"]) == (4, 64, 528)
+    # d = 64, 544 blocks of 128 rows: three per CU in one round (as at d = 128)
+    p = fa.fa_fwd_plan(2, 8, 4300, 64, fa.FA_BF16)
+    assert (p["waves"], p["block_k"], p["grid"]) == (4, 64, 544)
 
 
 @pytest.mark.parametrize("B,H,N,d,plan", [
@@ -261,7 +263,9 @@ def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_sh
     (4, 8, 4097, 128, (8, 128)),
     (1, 16, 4097, 128, (8, 128)),
     (2, 16, 4097, 64, (8, 128)),
-    (2, 8, 4129, 128, (4, 32)),      # 33 last rows: 528 blocks of 128 at three per CU
+    (2, 8, 4129, 128, (8, 128)),     # 33 last rows first: 139 us; 4 waves at three per CU 172 us
+    (2, 8, 4160, 128, (8, 128)),     # 64 last rows first: 142 us; 172 us
+    (2, 8, 4300, 128, (4, 32)),      # 204 last rows: 544 blocks of 128 at three per CU
     (8, 8, 4097, 128, (8, 128)),     # last rows first: 505 us; 4 waves 527 us, 8 waves with short blocks 527 us
     (2, 8, 16385, 128, (8, 128)),    # last rows first: 1.88 ms; 2.05 and 2.07 ms
     (16, 64, 2049, 128, (4, 32)),    # 1024 heads: 2.13 ms; 8 waves 2.27 ms, last rows first 2.33 ms

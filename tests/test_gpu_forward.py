@@ -283,7 +283,7 @@ def test_eight_wave_plan_sampled(gpu_lib, monkeypatch, dtype, d, N, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("B,H,N", [(5, 8, 2001), (2, 8, 4129)])
+@pytest.mark.parametrize("B,H,N", [(5, 8, 2001), (2, 8, 4300)])
 def test_three_per_cu_plan_sampled(gpu_lib, dtype, B, H, N):
     # grids just over one round of two 128-row workgroups per CU run on the 32-key-tile
     # kernel at three per CU (non-causal); ragged last query block and key tile
@@ -314,6 +314,9 @@ TAIL_FIRST = [
     (2, 4, 8193, 128, "fp16"),
     (2, 8, 4128, 128, "bf16"),    # 32 last rows
     (2, 8, 4113, 64, "bf16"),     # 17 last rows
+    (2, 8, 4160, 128, "bf16"),    # 64 last rows: two waves of the split-KV block
+    (2, 8, 4224, 128, "fp16"),    # 128 last rows: the whole split-KV block
+    (2, 8, 4196, 64, "bf16"),     # 100 last rows
 ]
 
 
@@ -375,7 +378,7 @@ def test_tail_first_not_taken_when_o_overlaps_an_input(gpu_lib, capfd, monkeypat
 
 IN_PLACE = [
     # (B, H, N, d, dtype, causal, FA_TILE): O written over Q on each kind of plan
-    (2, 8, 4129, 128, "bf16", False, ""),           # 4 waves, 32-key tiles, three per CU
+    (2, 8, 4300, 128, "bf16", False, ""),           # 4 waves, 32-key tiles, three per CU
     (1, 2, 1153, 128, "bf16", False, "128,32,4"),   # the last block's waves split its keys
     (2, 4, 2100, 64, "fp16", False, "256,128,8"),   # ping-pong
     (1, 4, 1500, 128, "bf16", True, ""),            # causal
