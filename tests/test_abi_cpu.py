@@ -572,6 +572,10 @@ def test_log_prints_the_plan_to_stderr(lib, monkeypatch, capfd):
     monkeypatch.setenv("FA_TILE", "128,64,4")
     _fwd(lib, B=4, H=32, N=16384, d=128)
     monkeypatch.delenv("FA_TILE")
+    # tail first (its partials go to O, so O must not overlap the inputs: distinct addresses)
+    far = [ctypes.c_void_p(a << 32) for a in range(1, 6)]
+    _fwd(lib, *far, B=2, H=8, N=4097, d=128)
+    _fwd(lib, B=2, H=8, N=4097, d=128)   # O over Q: the 8-wave grid with its short blocks
     monkeypatch.setenv("FA_LOG", "0")
     _fwd(lib, B=1, H=1, N=77, d=64)
     err = capfd.readouterr().err
@@ -581,6 +585,9 @@ def test_log_prints_the_plan_to_stderr(lib, monkeypatch, capfd):
     assert "fa_bwd: B=1 H=2 N=64 d=64 bf16" in err
     assert "fa_fwd_fp8: B=1 H=2 N=100 d=128" in err
     assert "Br=128 Bc=64 waves=4 grid=16384 lds=65536 (FA_TILE)" in err
+    assert ("fa_fwd: B=2 H=8 N=4097 Nk=4097 d=128 bf16 -> Br=256 Bc=128 waves=8 grid=256 lds=131072 "
+            "(the last 1 rows first: 16 key ranges per head, merged)") in err
+    assert "fa_fwd: B=2 H=8 N=4097 Nk=4097 d=128 bf16 -> Br=256 Bc=128 waves=8 grid=272 lds=131072\n" in err
     assert "N=77" not in err          # FA_LOG=0: silent
 
 
