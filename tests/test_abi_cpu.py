@@ -270,6 +270,10 @@ def test_plan_takes_three_workgroups_per_cu_for_a_grid_just_over_one_round_or_sh
     (2, 8, 16385, 128, (8, 128)),    # last rows first: 1.88 ms; 2.05 and 2.07 ms
     (16, 64, 2049, 128, (4, 32)),    # 1024 heads: 2.13 ms; 8 waves 2.27 ms, last rows first 2.33 ms
     (8, 16, 2049, 128, (4, 32)),     # 273 us; last rows first 285 us, 8 waves 290 us
+    (16, 16, 2049, 128, (4, 32)),    # 523 us; 8 waves (last rows first) 546 us
+    (2, 32, 4097, 128, (8, 128)),    # last rows first: 496 us; 4 waves at three per CU 522 us
+    (4, 32, 4097, 128, (4, 32)),     # 993 us; 8 waves (last rows first) 1002 us
+    (1, 32, 8193, 128, (8, 128)),    # last rows first: 940 us; 1028 us
     (1, 8, 4096, 128, (4, 64)),      # 256 blocks of 128, one per CU: 80 us; 8 waves 100 us
     (4, 16, 2048, 64, (8, 128)),     # 512 blocks of 256 (ping-pong): 84 us; 4 waves 86-87 us
 ])
